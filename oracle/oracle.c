@@ -1,0 +1,303 @@
+/*
+ * Exact softmax attention in fp64 on the CPU -- the correctness oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or calls
+ * this file; only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header or constant with the HIP kernels.
+ *
+ * What it computes (the plain, materialised definition, no tiling, no online
+ * rescaling):
+ *   - "FlashAttention: lightning-fast Transformer" (llmtrend.com), section on the
+ *     bottleneck of self-attention: Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V,
+ *     evaluated in its four listed steps (similarities, scaling, softmax, weighted
+ *     sum of V).  The scale is an argument; callers pass 1/sqrt(d) by default.
+ *   - "MHA tuning, part 1" (handbook ch.3), section "where is the memory bottleneck
+ *     of classic MHA": the eager form scores = Q K^T * scale, weights = softmax,
+ *     output = weights V, with the score tensor shaped [batch, heads, seq, seq].
+ *   - Same page, section "engineering implementation": the per-row log-sum-exp
+ *     statistic kept beside the output (natural log of the sum of exp of the
+ *     scaled, masked scores).
+ *   - Same page, section "notes in practice" (causal mask: future positions are
+ *     skipped).  Query i sees key j iff j <= i (square, top-left aligned).
+ *   - llmtrend.com, "numerical stability": subtract the row max before exp.
+ *   - "Flash Attention application" (jsqmd.com), section "Recomputation": the
+ *     backward does not keep P from the forward; here P is recomputed from the
+ *     inputs.  The gradient formulas are the calculus of the definition above
+ *     (the pages print none):
+ *       dV_j  = sum_i P_ij dO_i
+ *       dP_ij = dO_i . V_j
+ *       D_i   = sum_j P_ij dP_ij
+ *       dS_ij = P_ij (dP_ij - D_i)
+ *       dQ_i  = scale * sum_j dS_ij K_j
+ *       dK_j  = scale * sum_i dS_ij Q_i
+ *
+ * Layout: Q,K,V,O,dO,dQ,dK,dV are contiguous [B][H][N][d] arrays of double;
+ * LSE is [B][H][N].  Rows of one head are split across pthreads; each row's full
+ * score vector is formed (a row of the N x N matrix), so the result does not
+ * depend on the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_MAX_THREADS 256
+
+/* ------------------------------------------------------------------------ */
+/* forward                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* One query row: s_j = scale * q.k_j for visible j, P = softmax(s), o = P V,
+ * lse = m + log(sum exp(s - m)).  `s` is scratch of length N. */
+static void fwd_row(const double *q, const double *K, const double *V, long N,
+                    long d, double scale, int causal, long i, double *o,
+                    double *lse, double *s) {
+  long nvis = causal ? i + 1 : N; /* keys 0..nvis-1 are visible */
+  double m = -INFINITY;
+  for (long j = 0; j < nvis; ++j) {
+    double acc = 0.0;
+    for (long c = 0; c < d; ++c) acc += q[c] * K[j * d + c];
+    s[j] = scale * acc;
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (long j = 0; j < nvis; ++j) {
+    s[j] = exp(s[j] - m); /* unnormalised weight */
+    l += s[j];
+  }
+  for (long c = 0; c < d; ++c) o[c] = 0.0;
+  for (long j = 0; j < nvis; ++j) {
+    double p = s[j] / l;
+    for (long c = 0; c < d; ++c) o[c] += p * V[j * d + c];
+  }
+  *lse = m + log(l);
+}
+
+typedef struct {
+  const double *q, *k, *v;
+  long H, N, d;
+  double scale;
+  int causal;
+  const long *rows; /* flat row ids b*H*N + h*N + i */
+  long nrows;
+  double *o, *lse; /* per selected row: o[r*d..], lse[r] */
+  long r0, r1;
+} fwd_job;
+
+static void *fwd_worker(void *arg) {
+  fwd_job *J = (fwd_job *)arg;
+  double *s = (double *)malloc(sizeof(double) * (size_t)J->N);
+  if (!s) return (void *)1;
+  for (long r = J->r0; r < J->r1; ++r) {
+    long flat = J->rows[r];
+    long bh = flat / J->N, i = flat % J->N;
+    const double *Kh = J->k + bh * J->N * J->d;
+    const double *Vh = J->v + bh * J->N * J->d;
+    fwd_row(J->q + flat * J->d, Kh, Vh, J->N, J->d, J->scale, J->causal, i,
+            J->o + r * J->d, J->lse + r, s);
+  }
+  free(s);
+  return NULL;
+}
+
+static int clamp_threads(int t) {
+  if (t < 1) return 1;
+  if (t > ORACLE_MAX_THREADS) return ORACLE_MAX_THREADS;
+  return t;
+}
+
+/* Forward on a chosen set of query rows.  rows[r] = b*H*N + h*N + i.
+ * Returns 0 on success, nonzero on bad arguments or allocation failure. */
+int oracle_fwd_rows(const double *q, const double *k, const double *v, long B,
+                    long H, long N, long d, double scale, int causal,
+                    const long *rows, long nrows, double *o_rows,
+                    double *lse_rows, int nthreads) {
+  if (!q || !k || !v || !rows || !o_rows || !lse_rows) return 1;
+  if (B < 1 || H < 1 || N < 1 || d < 1 || nrows < 0) return 2;
+  for (long r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= B * H * N) return 3;
+  int T = clamp_threads(nthreads);
+  if (T > nrows) T = nrows > 0 ? (int)nrows : 1;
+  pthread_t th[ORACLE_MAX_THREADS];
+  fwd_job jobs[ORACLE_MAX_THREADS];
+  int err = 0;
+  for (int t = 0; t < T; ++t) {
+    fwd_job *J = &jobs[t];
+    J->q = q; J->k = k; J->v = v; J->H = H; J->N = N; J->d = d;
+    J->scale = scale; J->causal = causal; J->rows = rows; J->nrows = nrows;
+    J->o = o_rows; J->lse = lse_rows;
+    J->r0 = nrows * t / T; J->r1 = nrows * (t + 1) / T;
+  }
+  for (int t = 1; t < T; ++t)
+    if (pthread_create(&th[t], NULL, fwd_worker, &jobs[t])) err = 4;
+  if (fwd_worker(&jobs[0])) err = 5;
+  for (int t = 1; t < T; ++t) {
+    void *ret = NULL;
+    pthread_join(th[t], &ret);
+    if (ret) err = 5;
+  }
+  return err;
+}
+
+/* Forward over every row of every head. */
+int oracle_fwd(const double *q, const double *k, const double *v, long B,
+               long H, long N, long d, double scale, int causal, double *o,
+               double *lse, int nthreads) {
+  long total = B * H * N;
+  if (total < 1) return 2;
+  long *rows = (long *)malloc(sizeof(long) * (size_t)total);
+  if (!rows) return 5;
+  for (long r = 0; r < total; ++r) rows[r] = r;
+  int rc = oracle_fwd_rows(q, k, v, B, H, N, d, scale, causal, rows, total, o,
+                           lse, nthreads);
+  free(rows);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* backward, one head at a time, with the N x N matrices P and dS formed      */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const double *q, *k, *v, *dout; /* this head, [N][d] */
+  double *P, *dS;                 /* [N][N] */
+  double *dq, *dk, *dv;           /* this head, [N][d] */
+  long N, d;
+  double scale;
+  int causal;
+  int phase;
+  long a0, a1; /* row (phase 0, 2) or column (phase 1, 3) range */
+} bwd_job;
+
+static void *bwd_worker(void *arg) {
+  bwd_job *J = (bwd_job *)arg;
+  long N = J->N, d = J->d;
+  if (J->phase == 0) {
+    /* rows of P: recomputed from Q, K as in the forward */
+    for (long i = J->a0; i < J->a1; ++i) {
+      double *Pi = J->P + i * N;
+      long nvis = J->causal ? i + 1 : N;
+      double m = -INFINITY;
+      for (long j = 0; j < nvis; ++j) {
+        double acc = 0.0;
+        for (long c = 0; c < d; ++c) acc += J->q[i * d + c] * J->k[j * d + c];
+        Pi[j] = J->scale * acc;
+        if (Pi[j] > m) m = Pi[j];
+      }
+      double l = 0.0;
+      for (long j = 0; j < nvis; ++j) {
+        Pi[j] = exp(Pi[j] - m);
+        l += Pi[j];
+      }
+      for (long j = 0; j < nvis; ++j) Pi[j] /= l;
+      for (long j = nvis; j < N; ++j) Pi[j] = 0.0; /* masked: weight 0 */
+    }
+  } else if (J->phase == 1) {
+    /* dV_j = sum_i P_ij dO_i */
+    for (long j = J->a0; j < J->a1; ++j)
+      for (long c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (long i = 0; i < N; ++i) acc += J->P[i * N + j] * J->dout[i * d + c];
+        J->dv[j * d + c] = acc;
+      }
+  } else if (J->phase == 2) {
+    /* dP_ij = dO_i . V_j ; D_i = sum_j P_ij dP_ij ; dS = P (dP - D) ;
+     * dQ_i = scale * sum_j dS_ij K_j */
+    for (long i = J->a0; i < J->a1; ++i) {
+      double *dSi = J->dS + i * N;
+      const double *Pi = J->P + i * N;
+      for (long j = 0; j < N; ++j) {
+        double acc = 0.0;
+        for (long c = 0; c < d; ++c) acc += J->dout[i * d + c] * J->v[j * d + c];
+        dSi[j] = acc; /* dP for now */
+      }
+      double D = 0.0;
+      for (long j = 0; j < N; ++j) D += Pi[j] * dSi[j];
+      for (long j = 0; j < N; ++j) dSi[j] = Pi[j] * (dSi[j] - D);
+      for (long c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (long j = 0; j < N; ++j) acc += dSi[j] * J->k[j * d + c];
+        J->dq[i * d + c] = J->scale * acc;
+      }
+    }
+  } else {
+    /* dK_j = scale * sum_i dS_ij Q_i */
+    for (long j = J->a0; j < J->a1; ++j)
+      for (long c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (long i = 0; i < N; ++i) acc += J->dS[i * N + j] * J->q[i * d + c];
+        J->dk[j * d + c] = J->scale * acc;
+      }
+  }
+  return NULL;
+}
+
+static int run_phase(bwd_job *base, int phase, int T) {
+  pthread_t th[ORACLE_MAX_THREADS];
+  bwd_job jobs[ORACLE_MAX_THREADS];
+  int err = 0;
+  long N = base->N;
+  for (int t = 0; t < T; ++t) {
+    jobs[t] = *base;
+    jobs[t].phase = phase;
+    jobs[t].a0 = N * t / T;
+    jobs[t].a1 = N * (t + 1) / T;
+  }
+  for (int t = 1; t < T; ++t)
+    if (pthread_create(&th[t], NULL, bwd_worker, &jobs[t])) err = 4;
+  bwd_worker(&jobs[0]);
+  for (int t = 1; t < T; ++t) pthread_join(th[t], NULL);
+  return err;
+}
+
+/* Backward for a chosen set of heads.  heads[h] = b*H + h.  Outputs dq, dk, dv
+ * are [nheads][N][d] (one block per selected head, in the order given).
+ * The four phases run one after another; each needs the previous phase's
+ * matrices complete.  Returns 0 on success. */
+int oracle_bwd_heads(const double *q, const double *k, const double *v,
+                     const double *dout, long B, long H, long N, long d,
+                     double scale, int causal, const long *heads, long nheads,
+                     double *dq, double *dk, double *dv, int nthreads) {
+  if (!q || !k || !v || !dout || !heads || !dq || !dk || !dv) return 1;
+  if (B < 1 || H < 1 || N < 1 || d < 1 || nheads < 0) return 2;
+  for (long x = 0; x < nheads; ++x)
+    if (heads[x] < 0 || heads[x] >= B * H) return 3;
+  int T = clamp_threads(nthreads);
+  if (T > N) T = (int)N;
+  double *P = (double *)malloc(sizeof(double) * (size_t)N * (size_t)N);
+  double *dS = (double *)malloc(sizeof(double) * (size_t)N * (size_t)N);
+  if (!P || !dS) {
+    free(P);
+    free(dS);
+    return 5;
+  }
+  int err = 0;
+  for (long x = 0; x < nheads && !err; ++x) {
+    long off = heads[x] * N * d;
+    bwd_job base;
+    memset(&base, 0, sizeof base);
+    base.q = q + off; base.k = k + off; base.v = v + off; base.dout = dout + off;
+    base.P = P; base.dS = dS;
+    base.dq = dq + x * N * d; base.dk = dk + x * N * d; base.dv = dv + x * N * d;
+    base.N = N; base.d = d; base.scale = scale; base.causal = causal;
+    for (int phase = 0; phase < 4 && !err; ++phase) err = run_phase(&base, phase, T);
+  }
+  free(P);
+  free(dS);
+  return err;
+}
+
+/* Backward over every head. */
+int oracle_bwd(const double *q, const double *k, const double *v,
+               const double *dout, long B, long H, long N, long d, double scale,
+               int causal, double *dq, double *dk, double *dv, int nthreads) {
+  long nh = B * H;
+  if (nh < 1) return 2;
+  long *heads = (long *)malloc(sizeof(long) * (size_t)nh);
+  if (!heads) return 5;
+  for (long x = 0; x < nh; ++x) heads[x] = x;
+  int rc = oracle_bwd_heads(q, k, v, dout, B, H, N, d, scale, causal, heads, nh,
+                            dq, dk, dv, nthreads);
+  free(heads);
+  return rc;
+}

@@ -1,0 +1,310 @@
+"""Pins for the fp64 oracle: closed forms, a hand-derived worked example,
+invariants, brute force in extended precision, an independent tiled (online
+softmax) evaluation, library autograd and finite differences.
+
+Each check is chosen so that a plausible mistake in the oracle (a dropped scale,
+a wrong mask boundary, a transposed operand, a sign error in the softmax
+gradient, a missing max subtraction) fails at least one of them; the mutation
+tests at the end plant such mistakes in a copy of the oracle and assert that.
+"""
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# --------------------------------------------------------------------------
+# worked example derived by hand (tests/golden/tiny_n2_d2.json)
+# --------------------------------------------------------------------------
+
+def load_golden():
+    with open(os.path.join(GOLDEN, "tiny_n2_d2.json")) as f:
+        g = json.load(f)
+    as4 = lambda a: np.array(a, np.float64)[None, None]
+    return g, as4(g["q"]), as4(g["k"]), as4(g["v"]), as4(g["dout"])
+
+
+def test_golden_forward_noncausal():
+    g, q, k, v, _ = load_golden()
+    o, lse = oracle.fwd(q, k, v, g["scale"], False)
+    np.testing.assert_allclose(o[0, 0], g["noncausal"]["o"], atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], g["noncausal"]["lse"], atol=1e-12)
+
+
+def test_golden_forward_causal():
+    g, q, k, v, _ = load_golden()
+    o, lse = oracle.fwd(q, k, v, g["scale"], True)
+    np.testing.assert_allclose(o[0, 0], g["causal"]["o"], atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], g["causal"]["lse"], atol=1e-12)
+
+
+def test_golden_backward_noncausal():
+    g, q, k, v, do = load_golden()
+    dq, dk, dv = oracle.bwd(q, k, v, do, g["scale"], False)
+    np.testing.assert_allclose(dq[0, 0], g["noncausal"]["dq"], atol=1e-12)
+    np.testing.assert_allclose(dk[0, 0], g["noncausal"]["dk"], atol=1e-12)
+    np.testing.assert_allclose(dv[0, 0], g["noncausal"]["dv"], atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_values(causal):
+    B, H, N, d = 1, 2, 13, 8
+    q = rnd((B, H, N, d), 1)
+    v = rnd((B, H, N, d), 2)
+    k = np.broadcast_to(rnd((B, H, 1, d), 3), (B, H, N, d)).copy()
+    scale = 0.37
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    for i in range(N):
+        n_vis = i + 1 if causal else N
+        np.testing.assert_allclose(o[:, :, i], v[:, :, :n_vis].mean(axis=2), atol=1e-12)
+        s = scale * np.einsum("bhc,bhc->bh", q[:, :, i], k[:, :, 0])
+        np.testing.assert_allclose(lse[:, :, i], s + math.log(n_vis), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_key_returns_v_exactly(causal):
+    q, k, v = rnd((2, 3, 1, 16), 4), rnd((2, 3, 1, 16), 5), rnd((2, 3, 1, 16), 6)
+    o, lse = oracle.fwd(q, k, v, 0.25, causal)
+    assert np.array_equal(o, v)
+    np.testing.assert_allclose(lse[..., 0], 0.25 * (q[..., 0, :] * k[..., 0, :]).sum(-1), atol=1e-13)
+
+
+def test_causal_row0_is_v0():
+    q, k, v = rnd((1, 2, 9, 8), 7), rnd((1, 2, 9, 8), 8), rnd((1, 2, 9, 8), 9)
+    o, lse = oracle.fwd(q, k, v, 0.5, True)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.5 * (q[:, :, 0] * k[:, :, 0]).sum(-1), atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    # with V = identity (N = d) the output rows are the softmax rows themselves
+    N = 12
+    q, k = rnd((1, 1, N, N), 10), rnd((1, 1, N, N), 11)
+    v = np.eye(N)[None, None]
+    p, _ = oracle.fwd(q, k, v, 0.3, causal)
+    p = p[0, 0]
+    assert (p >= 0).all()
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+    if causal:
+        assert np.count_nonzero(np.triu(p, 1)) == 0
+        assert (np.diag(p) > 0).all()
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("mag", [1.0, 12.0])
+def test_lse_and_output_match_50_digit_brute_force(N, causal, mag):
+    d = 4
+    q, k, v = rnd((1, 1, N, d), 20 + N, mag), rnd((1, 1, N, d), 30 + N, mag), rnd((1, 1, N, d), 40 + N)
+    scale = 1 / math.sqrt(d)
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    mpmath.mp.dps = 50
+    for i in range(N):
+        js = range(i + 1) if causal else range(N)
+        # no max subtraction: plain log of the plain sum, at 50 digits
+        e = {j: mpmath.exp(mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[0, 0, i, c]) * mpmath.mpf(k[0, 0, j, c])
+                                                          for c in range(d))) for j in js}
+        tot = mpmath.fsum(e.values())
+        assert abs(float(mpmath.log(tot)) - lse[0, 0, i]) <= 1e-12 * max(1.0, abs(lse[0, 0, i]))
+        for c in range(d):
+            ref = mpmath.fsum(e[j] * mpmath.mpf(v[0, 0, j, c]) for j in js) / tot
+            assert abs(float(ref) - o[0, 0, i, c]) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_invariance(causal):
+    q, k, v = rnd((1, 2, 10, 6), 50), rnd((1, 2, 10, 6), 51), rnd((1, 2, 10, 6), 52)
+    u = rnd((1, 2, 1, 6), 53)
+    o1, l1 = oracle.fwd(q, k, v, 0.4, causal)
+    o2, l2 = oracle.fwd(q, k + u, v, 0.4, causal)
+    np.testing.assert_allclose(o2, o1, atol=1e-12)
+    np.testing.assert_allclose(l2, l1 + 0.4 * np.einsum("bhnc,bhkc->bhn", q, u), atol=1e-12)
+
+
+def test_permutation_equivariance_noncausal():
+    q, k, v = rnd((1, 1, 11, 5), 60), rnd((1, 1, 11, 5), 61), rnd((1, 1, 11, 5), 62)
+    perm = np.random.default_rng(63).permutation(11)
+    o, lse = oracle.fwd(q, k, v, 0.7, False)
+    o2, lse2 = oracle.fwd(q, k[:, :, perm], v[:, :, perm], 0.7, False)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    o3, lse3 = oracle.fwd(q[:, :, perm], k, v, 0.7, False)
+    np.testing.assert_allclose(o3, o[:, :, perm], atol=1e-12)
+    np.testing.assert_allclose(lse3, lse[:, :, perm], atol=1e-12)
+
+
+def test_huge_scores_stay_finite():
+    q, k, v = rnd((1, 1, 16, 8), 70, 40.0), rnd((1, 1, 16, 8), 71, 40.0), rnd((1, 1, 16, 8), 72)
+    o, lse = oracle.fwd(q, k, v, 1.0, False)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    assert (np.abs(o) <= np.abs(v).max(axis=2, keepdims=True) + 1e-12).all()
+
+
+# --------------------------------------------------------------------------
+# an independent evaluation: block-wise online softmax (running max, running
+# sum, rescaling of the partial output), as the tuning handbook's
+# "engineering implementation" section describes, written here in numpy
+# --------------------------------------------------------------------------
+
+def tiled_online(q, k, v, scale, causal, block):
+    B, H, N, d = q.shape
+    o = np.zeros_like(q)
+    lse = np.full((B, H, N), -np.inf)
+    for i0 in range(0, N, block):
+        i1 = min(N, i0 + block)
+        m = np.full((B, H, i1 - i0, 1), -np.inf)
+        l = np.zeros((B, H, i1 - i0, 1))
+        acc = np.zeros((B, H, i1 - i0, d))
+        for j0 in range(0, N, block):
+            j1 = min(N, j0 + block)
+            s = scale * q[:, :, i0:i1] @ np.swapaxes(k[:, :, j0:j1], -1, -2)
+            if causal:
+                ii = np.arange(i0, i1)[:, None]
+                jj = np.arange(j0, j1)[None, :]
+                s = np.where(jj <= ii, s, -np.inf)
+            bm = s.max(-1, keepdims=True)
+            m_new = np.maximum(m, bm)
+            safe = np.where(np.isfinite(m_new), m_new, 0.0)
+            p = np.exp(s - safe)
+            alpha = np.exp(m - safe)
+            l = alpha * l + p.sum(-1, keepdims=True)
+            acc = alpha * acc + p @ v[:, :, j0:j1]
+            m = m_new
+        o[:, :, i0:i1] = acc / l
+        lse[:, :, i0:i1] = (m + np.log(l))[..., 0]
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,block", [(64, 16), (77, 16), (33, 64)])
+def test_online_tiled_equals_plain(causal, N, block):
+    q, k, v = rnd((2, 2, N, 16), 80), rnd((2, 2, N, 16), 81), rnd((2, 2, N, 16), 82)
+    o, lse = oracle.fwd(q, k, v, 0.25, causal)
+    o2, lse2 = tiled_online(q, k, v, 0.25, causal, block)
+    np.testing.assert_allclose(o, o2, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# library routine: torch fp64 CPU, forward and autograd backward
+# --------------------------------------------------------------------------
+
+def torch_reference(q, k, v, dout, scale, causal):
+    import torch
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    Q, K, V = t(q), t(k), t(v)
+    s = torch.matmul(Q, K.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        N = q.shape[2]
+        mask = torch.ones(N, N, dtype=torch.bool).triu(1)
+        s = s.masked_fill(mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    o = torch.matmul(torch.softmax(s, dim=-1), V)
+    o.backward(torch.tensor(dout, dtype=torch.float64))
+    return o.detach().numpy(), lse.detach().numpy(), Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_fp64_autograd(causal):
+    shape = (2, 3, 40, 16)
+    q, k, v, do = (rnd(shape, 90 + i) for i in range(4))
+    scale = 1 / math.sqrt(16)
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    dq, dk, dv = oracle.bwd(q, k, v, do, scale, causal)
+    to, tl, tdq, tdk, tdv = torch_reference(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(o, to, atol=1e-12)
+    np.testing.assert_allclose(lse, tl, atol=1e-12)
+    np.testing.assert_allclose(dq, tdq, atol=1e-12)
+    np.testing.assert_allclose(dk, tdk, atol=1e-12)
+    np.testing.assert_allclose(dv, tdv, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# backward: finite differences of L = sum(dO * O), and invariants
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d", [(1, 3), (5, 4), (8, 2)])
+def test_backward_central_differences(causal, N, d):
+    q, k, v, do = (rnd((1, 1, N, d), 100 + i + 10 * N) for i in range(4))
+    scale = 0.6
+    dq, dk, dv = oracle.bwd(q, k, v, do, scale, causal)
+    loss = lambda q_, k_, v_: float((oracle.fwd(q_, k_, v_, scale, causal)[0] * do).sum())
+    h = 1e-6
+    for which, grad in (("q", dq), ("k", dk), ("v", dv)):
+        fd = np.zeros_like(grad)
+        for idx in np.ndindex(q.shape[2:]):
+            args = {"q": q, "k": k, "v": v}
+            plus = {a: b.copy() for a, b in args.items()}
+            minus = {a: b.copy() for a, b in args.items()}
+            plus[which][(0, 0) + idx] += h
+            minus[which][(0, 0) + idx] -= h
+            fd[(0, 0) + idx] = (loss(plus["q"], plus["k"], plus["v"]) -
+                                loss(minus["q"], minus["k"], minus["v"])) / (2 * h)
+        np.testing.assert_allclose(grad, fd, atol=2e-8, rtol=1e-6, err_msg=which)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    q, k, v, do = (rnd((1, 2, 24, 8), 120 + i) for i in range(4))
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.35, causal)
+    # dS rows sum to zero, so the key gradients sum to zero over keys
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    # P rows sum to one, so dV summed over keys equals dO summed over queries
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+    if causal:
+        # query 0 sees only key 0: its softmax is constant, so its gradient vanishes
+        np.testing.assert_allclose(dq[:, :, 0], 0.0, atol=1e-14)
+        # the last key is seen only by the last query: dV_last = P_last,last * dO_last
+        _, lse = oracle.fwd(q, k, v, 0.35, causal)
+        p_ll = np.exp(0.35 * (q[:, :, -1] * k[:, :, -1]).sum(-1) - lse[:, :, -1])
+        np.testing.assert_allclose(dv[:, :, -1], p_ll[..., None] * do[:, :, -1], atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# entry points agree with each other
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_and_heads_subsets_match_full(causal):
+    B, H, N, d = 2, 3, 21, 8
+    q, k, v, do = (rnd((B, H, N, d), 130 + i) for i in range(4))
+    o, lse = oracle.fwd(q, k, v, 0.3, causal, threads=1)
+    rows = np.array([0, 5, N - 1, N, 2 * H * N - 1, 3 * N + 7])
+    o_r, l_r = oracle.fwd_rows(q, k, v, 0.3, causal, rows, threads=3)
+    assert np.array_equal(o_r, o.reshape(-1, d)[rows])
+    assert np.array_equal(l_r, lse.reshape(-1)[rows])
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.3, causal, threads=4)
+    heads = np.array([4, 0])
+    hq, hk, hv = oracle.bwd_heads(q, k, v, do, 0.3, causal, heads, threads=1)
+    for x, hh in enumerate(heads):
+        assert np.array_equal(hq[x], dq.reshape(B * H, N, d)[hh])
+        assert np.array_equal(hk[x], dk.reshape(B * H, N, d)[hh])
+        assert np.array_equal(hv[x], dv.reshape(B * H, N, d)[hh])
+
+
+def test_bad_arguments_are_rejected():
+    q = np.zeros((1, 1, 4, 2))
+    with pytest.raises(RuntimeError):
+        oracle.fwd_rows(q, q, q, 1.0, False, [4])
+    with pytest.raises(RuntimeError):
+        oracle.bwd_heads(q, q, q, q, 1.0, False, [1])

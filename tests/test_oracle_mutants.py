@@ -1,0 +1,62 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one of them."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    # forward
+    "dropped_scale": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "causal_excludes_diagonal": ("long nvis = causal ? i + 1 : N;", "long nvis = causal ? i : N;"),
+    "causal_sees_one_future_key": ("long nvis = causal ? i + 1 : N; /* keys", "long nvis = causal ? (i + 2 < N ? i + 2 : N) : N; /* keys"),
+    "no_max_subtraction": ("s[j] = exp(s[j] - m); /* unnormalised weight */", "s[j] = exp(s[j]); /* unnormalised weight */"),
+    "lse_without_max": ("*lse = m + log(l);", "*lse = log(l);"),
+    "value_transposed": ("o[c] += p * V[j * d + c];", "o[c] += p * V[c * d + j % d];"),
+    # backward
+    "softmax_grad_sign": ("dSi[j] = Pi[j] * (dSi[j] - D);", "dSi[j] = Pi[j] * (dSi[j] + D);"),
+    "dk_uses_k": ("acc += J->dS[i * N + j] * J->q[i * d + c];", "acc += J->dS[i * N + j] * J->k[i * d + c];"),
+    "dq_missing_scale": ("J->dq[i * d + c] = J->scale * acc;", "J->dq[i * d + c] = acc;"),
+    "dv_uses_transposed_p": ("acc += J->P[i * N + j] * J->dout[i * d + c];", "acc += J->P[j * N + i] * J->dout[i * d + c];"),
+}
+
+PINS = [
+    lambda: pins.test_golden_forward_noncausal(),
+    lambda: pins.test_golden_forward_causal(),
+    lambda: pins.test_golden_backward_noncausal(),
+    lambda: pins.test_identical_keys_give_mean_of_values(True),
+    lambda: pins.test_causal_row0_is_v0(),
+    lambda: pins.test_probability_rows_sum_to_one(True),
+    lambda: pins.test_lse_and_output_match_50_digit_brute_force(5, True, 12.0),
+    lambda: pins.test_huge_scores_stay_finite(),
+    lambda: pins.test_backward_central_differences(True, 5, 4),
+    lambda: pins.test_backward_invariants(True),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", str(mutant), "-o", str(lib), "-lm"])
+    saved_lib, saved_path = oracle._lib, oracle._LIB
+    monkeypatch.setattr(oracle, "_lib", None)
+    monkeypatch.setattr(oracle, "_LIB", str(lib))
+    monkeypatch.setattr(oracle, "build", lambda force=False: str(lib))
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, RuntimeError, FloatingPointError, ValueError, OverflowError):
+            caught.append(pin)
+    assert caught, f"no pin caught mutant {name}"
