@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Attention throughput on one MI355X: fused forward + recompute backward.
+
+One step = one pass of the whole hot path over one batch: fa_fwd (O, LSE) then
+fa_bwd (D = rowsum(dO*O), the main backward kernel, dQ conversion) on the
+causal workload B=4, H=32, N=8192, d=128, bf16, with Q, K, V, dO i.i.d. N(0,1)
+from a fixed seed, all resident in HBM before timing starts.
+
+FLOP convention: 4*B*H*N^2*d for the forward, halved when causal; the backward
+counts 2.5x the forward.  `value` is (forward + backward FLOP) / step time.
+
+Per-kernel figures are measured live with HIP events recorded on the stream the
+kernels run on.  The CPU baseline times the fp64 oracle on a bounded sample of
+the same workload (one head: the forward over every row, the backward over the
+whole head) on the host's cores.
+
+Extra modes: --copy-ref MiB runs a plain device copy of known size (the
+reference for scaling hardware byte counters); --check compares a few sampled
+rows against the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+WORKLOAD = dict(name="c3_fwd_bwd_causal_n8192_d128_bf16", B=4, H=32, N=8192, d=128, dtype="bf16",
+                causal=True)
+
+
+def nominal_flop(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+    return f, 2.5 * f
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_inputs(w, device):
+    import numpy as np
+    import torch
+    import fa_inputs
+    seed = fa_inputs.CONFIGS["c3_bwd_causal_n8192_d128_bf16"]["seed"]
+    bits = fa_inputs.qkv_bits(w["B"], w["H"], w["N"], w["d"], w["dtype"], seed, with_dout=True)
+    tdt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float16
+    tens = [torch.from_numpy(b.view(np.int16)).view(tdt).to(device) for b in bits]
+    return bits, tens
+
+
+def cpu_baseline(bits, w, max_bwd_n):
+    """fp64 oracle on one head of the workload: forward over all rows, backward over the head."""
+    import numpy as np
+    import fa_inputs
+    import oracle
+    threads = oracle.default_threads()
+    N, d, causal = w["N"], w["d"], w["causal"]
+    scale = float(np.float32(1 / math.sqrt(d)))
+    sub = [fa_inputs.widen(x[0:1, 0:1], w["dtype"]) for x in bits]
+    rows = np.arange(N)
+    t0 = time.perf_counter()
+    oracle.fwd_rows(*sub[:3], scale, causal, rows, threads=threads)
+    t_fwd = time.perf_counter() - t0
+    f_fwd, f_bwd = nominal_flop(1, 1, N, d, causal)
+    flop, secs = f_fwd, t_fwd
+    sample = f"head (0,0): forward over all {N} rows"
+    if N <= max_bwd_n:
+        t0 = time.perf_counter()
+        oracle.bwd_heads(*sub, scale, causal, [0], threads=threads)
+        t_bwd = time.perf_counter() - t0
+        flop += f_bwd
+        secs += t_bwd
+        sample += f" ({t_fwd:.1f} s) + backward of the whole head ({t_bwd:.1f} s)"
+    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample + f"; nominal FLOP {flop:.3e} in {secs:.1f} s"}
+
+
+def copy_ref(mib, device):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_ref_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-bwd-max-n", type=int, default=8192,
+                    help="largest N for which the CPU baseline includes the backward")
+    ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB")
+    ap.add_argument("--fwd-only", action="store_true", help="time only the forward (diagnostics)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the kernels shard by head or batch with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_21_amd as fa
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    if args.copy_ref:
+        copy_ref(args.copy_ref, device)
+        return
+
+    w = WORKLOAD
+    B, H, N, d, causal = w["B"], w["H"], w["N"], w["d"], w["causal"]
+    log(f"[bench] generating inputs {w['name']}")
+    bits, (q, k, v, do) = make_inputs(w, device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=device)
+    scale = 1 / math.sqrt(d)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if not args.fwd_only:
+            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, ws, stream)
+            if ev is not None:
+                ev[2].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs] if not args.fwd_only else [0.0]
+    f_fwd, f_bwd = nominal_flop(B, H, N, d, causal)
+    ms_step = wall * 1e3 / args.steps
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    total_flop = f_fwd + (0 if args.fwd_only else f_bwd)
+    fwd_tf = f_fwd / (fwd_avg * 1e-3) / 1e12
+    bwd_tf = f_bwd / (bwd_avg * 1e-3) / 1e12 if not args.fwd_only else None
+    log(f"[bench] fwd {fwd_avg:.3f} ms ({fwd_tf:.0f} TFLOP/s)"
+        + ("" if args.fwd_only else f"  bwd {bwd_avg:.3f} ms ({bwd_tf:.0f} TFLOP/s)"))
+
+    roofline = {"kernel": "fwd_kernel (fa_fwd, one launch per step)", "bound": "mfma",
+                "achieved": fwd_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": fwd_tf / PEAK_BF16_TFLOPS, "traffic": None,
+                "avg_launch_ms": fwd_avg, "algorithmic_flop_per_launch": f_fwd}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        cpu = cpu_baseline(bits, w, args.cpu_bwd_max_n)
+
+    out = {
+        "metric": "attention TFLOPS and % of MI355X bf16 MFMA peak, fwd/bwd, N=1k-32k, d=128",
+        "value": total_flop / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: i.i.d. N(0,1) Q, K, V, dO from a fixed seed (no datasets or weights)",
+        "config": {"workload": w["name"] if not args.fwd_only else w["name"] + " (forward only)",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal, "pass": "fwd+bwd" if not args.fwd_only else "fwd",
+                   "flop_per_step": total_flop},
+        "fwd_ms": fwd_avg, "bwd_ms": bwd_avg if not args.fwd_only else None,
+        "fwd_tflops": fwd_tf, "bwd_tflops": bwd_tf,
+        "fwd_frac_of_peak": fwd_tf / PEAK_BF16_TFLOPS,
+        "bwd_frac_of_peak": (bwd_tf / PEAK_BF16_TFLOPS) if bwd_tf else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

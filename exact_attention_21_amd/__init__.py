@@ -1,0 +1,173 @@
+"""Python binding of the gfx950 fused-attention library (libfa.so).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their data pointers and torch's current HIP stream are handed to
+the C ABI declared in include/fa.h, and every step of the computation runs in
+the library's kernels.  There is no fallback: if libfa.so is missing or the
+device is not gfx950 the calls raise.
+
+Names mirror the C ABI: fa_fwd, fa_bwd, fa_bwd_workspace_size, fa_fwd_plan,
+fa_bwd_plan, fa_status_str.  fwd() and bwd() are conveniences that allocate the
+outputs (and the backward workspace) with torch and call fa_fwd / fa_bwd.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_F16, FA_BF16 = 0, 1
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {fa_status_str(status)}")
+        self.status = status
+
+
+class fa_plan_t(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("threads", ctypes.c_int),
+                ("grid", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("xcd_grouped", ctypes.c_int)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (built by exact_attention_21_amd.build); raises if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_21_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp]
+        L.fa_fwd.restype = I
+        L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp, Z, vp]
+        L.fa_bwd.restype = I
+        L.fa_bwd_workspace_size.argtypes = [I, I, I, I]
+        L.fa_bwd_workspace_size.restype = Z
+        L.fa_fwd_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(fa_plan_t)]
+        L.fa_fwd_plan.restype = I
+        L.fa_bwd_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(fa_plan_t)]
+        L.fa_bwd_plan.restype = I
+        L.fa_status_str.argtypes = [I]
+        L.fa_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def fa_status_str(status: int) -> str:
+    return lib().fa_status_str(int(status)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"only float16 / bfloat16 tensors are supported, got {t.dtype}")
+
+
+def _check_qkv_like(name, t, ref):
+    if t.device != ref.device or t.dtype != ref.dtype or t.shape != ref.shape:
+        raise ValueError(f"{name} must match q in device, dtype and shape")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def fa_fwd_plan(B, H, N, d, causal, dtype) -> fa_plan_t:
+    plan = fa_plan_t()
+    rc = lib().fa_fwd_plan(B, H, N, d, int(causal), int(dtype), ctypes.byref(plan))
+    if rc:
+        raise FaError("fa_fwd_plan", rc)
+    return plan
+
+
+def fa_bwd_plan(B, H, N, d, causal, dtype) -> fa_plan_t:
+    plan = fa_plan_t()
+    rc = lib().fa_bwd_plan(B, H, N, d, int(causal), int(dtype), ctypes.byref(plan))
+    if rc:
+        raise FaError("fa_bwd_plan", rc)
+    return plan
+
+
+def fa_bwd_workspace_size(B, H, N, d) -> int:
+    return int(lib().fa_bwd_workspace_size(B, H, N, d))
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
+    """Forward into caller-provided o ([B,H,N,d], q's dtype) and lse ([B,H,N] fp32)."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_qkv_like(name, t, q)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be contiguous float32 [B, H, N] on q's device")
+    rc = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                      int(bool(causal)), _dtype_code(q), _stream(stream))
+    if rc:
+        raise FaError("fa_fwd", rc)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool, workspace,
+           stream=None) -> None:
+    """Backward into caller-provided dq, dk, dv; workspace is a uint8 device tensor."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_qkv_like(name, t, q)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    if not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                      _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
+                      _ptr(workspace), ctypes.c_size_t(nbytes), _stream(stream))
+    if rc:
+        raise FaError("fa_bwd", rc)
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None):
+    """Returns (o, lse) for q, k, v of shape [B, H, N, d]."""
+    import torch
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, default_scale(d) if scale is None else scale, causal)
+    return o, lse
+
+
+def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, workspace=None):
+    """Returns (dq, dk, dv); o and lse are the forward's outputs."""
+    import torch
+    B, H, N, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, default_scale(d) if scale is None else scale, causal,
+           workspace)
+    return dq, dk, dv

@@ -1,0 +1,64 @@
+"""Compile the gfx950 HIP sources into the in-tree shared library libfa.so.
+
+Every translation unit is compiled with hipcc for gfx950 only; packed fp32 VALU
+instructions are disabled for device code.  Objects are built in parallel and
+linked with hipcc into exact_attention_21_amd/libfa.so.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libfa.so")
+BUILD_DIR = os.path.join(PKG, "_build")
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found; the library needs ROCm's hipcc to build")
+
+
+def compile_flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+            "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
+            # no packed fp32 VALU instructions in device code
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+
+    def one(src: str) -> str:
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        noise = "is not a recognized feature for this target"
+        err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    tmp = LIB + ".tmp"
+    subprocess.check_call([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,182 @@
+// C-ABI layer: argument validation, launch planning, device gating and kernel
+// launches for the fused attention library.  No allocation, no global mutable
+// state apart from a per-device "is gfx950" cache.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return FA_OK;
+    if (c == 2) return FA_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FA_OK : FA_ERR_DEVICE;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int H, int N, int d, int causal, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  const long double elems = (long double)B * H * N * (d > 0 ? d : 1);
+  if (elems > 4.0e18L) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  return FA_OK;
+}
+
+// Query rows per forward workgroup = 128 * qb.
+int fwd_qb(int N, int d) {
+  (void)d;
+  return N > 128 ? 2 : 1;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char *fa_status_str(int s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer argument";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1; element count too large)";
+    case FA_ERR_HEAD_DIM: return "head dim must be 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be FA_F16 (0) or FA_BF16 (1)";
+    case FA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "backward workspace too small";
+    case FA_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_ARG: return "scale must be finite and > 0; causal must be 0 or 1";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *plan) {
+  if (!plan) return FA_ERR_NULL;
+  const int rc = check_common(B, H, N, d, causal, dtype);
+  if (rc) return rc;
+  const int qb = fwd_qb(N, d);
+  const int bm = 128 * qb;
+  const int bn = d == 128 ? fa::FWD_BN_D128 : fa::FWD_BN_D64;
+  const long long nq = (N + bm - 1) / bm;
+  const long long grid = nq * B * H;
+  if (grid > 0x7fffffffLL) return FA_ERR_SHAPE;
+  plan->block_m = bm;
+  plan->block_n = bn;
+  plan->threads = 256;
+  plan->grid = (int)grid;
+  plan->lds_bytes = 2 * bn * ((d * 2 + 16) + (d * 2 + 64));
+  plan->xcd_grouped = ((long long)B * H) % 8 == 0;
+  return FA_OK;
+}
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+           int N, int d, float scale, int causal, int dtype, void *stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_plan_t plan;
+  int rc = fa_fwd_plan(B, H, N, d, causal, dtype, &plan);
+  if (rc) return rc;
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.N = N;
+  p.n_qtiles = (N + plan.block_m - 1) / plan.block_m;
+  p.xcd_grouped = plan.xcd_grouped;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_fwd(p, dtype, d, causal, plan.block_m / 128, plan.grid,
+                                      reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (check_common(B, H, N, d, 0, FA_BF16) != FA_OK) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int fa_bwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *plan) {
+  if (!plan) return FA_ERR_NULL;
+  const int rc = check_common(B, H, N, d, causal, dtype);
+  if (rc) return rc;
+  const long long nk = (N + fa::BWD_BN - 1) / fa::BWD_BN;
+  const long long grid = nk * B * H;
+  if (grid > 0x7fffffffLL) return FA_ERR_SHAPE;
+  plan->block_m = fa::BWD_BM;
+  plan->block_n = fa::BWD_BN;
+  plan->threads = 256;
+  plan->grid = (int)grid;
+  const int qs = d * 2 + 16, stage = 2 * fa::BWD_BM * qs + 2 * fa::BWD_BM * 4;
+  plan->lds_bytes = 2 * stage + fa::BWD_BN * (d * 2 + 64) + fa::BWD_BN * (fa::BWD_BM * 2 + 64);
+  plan->xcd_grouped = ((long long)B * H) % 8 == 0;
+  return FA_OK;
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
+           void *stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  fa_plan_t plan;
+  int rc = fa_bwd_plan(B, H, N, d, causal, dtype, &plan);
+  if (rc) return rc;
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  const void *ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void *ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+  const size_t rows = (size_t)B * H * N;
+  char *ws = static_cast<char *>(workspace);
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dq_acc = reinterpret_cast<float *>(ws);
+  p.dws = reinterpret_cast<float *>(ws + align256(rows * d * sizeof(float)));
+  p.N = N;
+  p.n_ktiles = (N + fa::BWD_BN - 1) / fa::BWD_BN;
+  p.xcd_grouped = plan.xcd_grouped;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_bwd(p, dtype, d, causal, plan.grid, (long)rows,
+                                      reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+/*
+ * Fused exact softmax attention for AMD Instinct MI355X (gfx950) -- C ABI.
+ *
+ * The operation (llmtrend.com page "FlashAttention", section on the bottleneck
+ * of self-attention, and its four listed steps):
+ *     O = softmax(Q K^T * scale [+ causal mask]) V
+ * computed as one fused, tiled kernel: each workgroup keeps a block of query
+ * rows on chip, streams K/V tiles through LDS and runs an online softmax (a
+ * running row max and running row sum, rescaling the partial output; MHA tuning
+ * handbook ch.3, sections "core idea" and "engineering implementation"), so the
+ * N x N score matrix never reaches HBM.  The forward also writes the per-row
+ * log-sum-exp (the same section's `lse` statistic), and the backward recomputes
+ * the probabilities from it instead of storing them ("Flash Attention
+ * application", section "Recomputation").
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are device pointers to contiguous row-major [B][H][N][d] arrays of
+ *     the 16-bit element type `dtype` (handbook ch.3 pseudocode layout
+ *     [batch, num_heads, seq_len, head_dim]; inputs must be contiguous as the
+ *     FA1-vs-FA2 page's troubleshooting section requires).  LSE and D are fp32
+ *     [B][H][N].  Every pointer must be 16-byte aligned.
+ *   - The caller owns all memory.  The library allocates nothing; the backward
+ *     takes a caller-provided workspace of fa_bwd_workspace_size() bytes.
+ *   - Only fp16 and bf16 are accepted ("Flash Attention application",
+ *     recommended configuration: FP16/BF16 only), accumulation is fp32.
+ *   - head_dim d must be 64 or 128.  Any N >= 1 is accepted; ragged tails are
+ *     masked inside the kernels.
+ *   - scale must be finite and > 0 (the pages use 1/sqrt(d_k)).
+ *   - causal = 1 applies the lower-triangular mask of a square attention
+ *     matrix: query i sees key j iff j <= i (handbook ch.3, notes on the causal
+ *     mask: future positions are skipped); fully masked tiles are never loaded.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL =
+ *     the null stream).  The return value reports argument and launch errors
+ *     only; execution errors surface at the caller's next synchronisation.  No
+ *     exception or abort crosses the ABI.  There is no global mutable state, so
+ *     concurrent calls on different streams are safe.
+ *   - The device current at the call must be a gfx950 GPU, else FA_ERR_DEVICE
+ *     (there is no fallback path).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or the element count overflows */
+  FA_ERR_HEAD_DIM = 3,  /* d not in {64, 128} */
+  FA_ERR_DTYPE = 4,     /* dtype not FA_F16 / FA_BF16 */
+  FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = 6, /* backward workspace too small */
+  FA_ERR_DEVICE = 7,    /* current device is not gfx950, or no device */
+  FA_ERR_LAUNCH = 8,    /* the HIP runtime rejected a kernel launch */
+  FA_ERR_ARG = 9        /* scale not finite and positive, or causal not 0/1 */
+} fa_status_t;
+
+/*
+ * Forward.  Inputs q, k, v: [B][H][N][d] in `dtype`.  Outputs: o [B][H][N][d] in
+ * `dtype` (rounded to nearest even from fp32), lse [B][H][N] fp32, the natural
+ * log of the sum over visible keys of exp(scale * q_i . k_j).
+ * Nothing is written when the call returns an error.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void *stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: an fp32 dQ accumulator [B][H][N][d]
+ * and D = rowsum(dO * O) fp32 [B][H][N], each 256-byte aligned.  Returns 0 for
+ * invalid shapes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward with recomputation ("Flash Attention application", section
+ * "Recomputation"; its v2 section on re-parallelising the backward kernel).
+ * Inputs: q, k, v, o (the forward's output), dout = dL/dO, all [B][H][N][d] in
+ * `dtype`; lse [B][H][N] fp32 from fa_fwd with the same scale and causal flag.
+ * Outputs: dq, dk, dv [B][H][N][d] in `dtype`.  The gradients are those of the
+ * definition above:
+ *   P = softmax(scale Q K^T [mask]), dV = P^T dO, dP = dO V^T,
+ *   D_i = rowsum(dO_i * O_i), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ * dK and dV are bitwise reproducible; dQ is accumulated with fp32 atomics and
+ * may differ run to run in the last bits.
+ * `workspace` must hold fa_bwd_workspace_size(B,H,N,d) bytes (16-byte aligned);
+ * its contents on entry do not matter and are clobbered.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const void *dout, const float *lse, void *dq, void *dk, void *dv,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Launch plan of a forward call (host-only, no GPU needed). */
+typedef struct {
+  int block_m;          /* query rows per workgroup */
+  int block_n;          /* keys per K/V tile */
+  int threads;          /* threads per workgroup */
+  int grid;             /* workgroups (1-D grid) */
+  int lds_bytes;        /* LDS per workgroup */
+  int xcd_grouped;      /* 1 if heads are grouped per XCD */
+} fa_plan_t;
+
+/* Fills *plan for a forward with these arguments; returns a status code
+ * (argument checks only, no device check). */
+int fa_fwd_plan(int B, int H, int N, int d, int causal, int dtype,
+                fa_plan_t *plan);
+
+/* Fills *plan for the main backward kernel (block_m = query rows per inner
+ * step, block_n = keys per workgroup). */
+int fa_bwd_plan(int B, int H, int N, int d, int causal, int dtype,
+                fa_plan_t *plan);
+
+/* Static description of a status code. */
+const char *fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

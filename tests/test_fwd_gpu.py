@@ -1,0 +1,149 @@
+"""Forward parity on the GPU: the HIP kernel against the fp64 oracle on the
+same seeded inputs.  Small shapes are compared element by element over every
+output; the full-size workloads on sampled rows the oracle computes one by one.
+Tolerances: O max-abs <= 2e-2 (bf16) / 4e-3 (fp16), LSE max-abs <= 1e-3."""
+import math
+
+import numpy as np
+import pytest
+
+import exact_attention_21_amd as fa
+import fa_inputs
+import oracle
+from tests.helpers import TOL_LSE, TOL_O, max_abs, say, to_device, to_host_f64, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(qb, kb, vb, dtype, causal, device, scale=None):
+    q, k, v = (to_device(x, dtype, device) for x in (qb, kb, vb))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    import torch
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_full(qb, kb, vb, dtype, causal, device, scale=None):
+    B, H, N, d = qb.shape
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    o, lse = run_fwd(qb, kb, vb, dtype, causal, device, scale)
+    q64, k64, v64 = (fa_inputs.widen(x, dtype) for x in (qb, kb, vb))
+    ro, rl = oracle.fwd(q64, k64, v64, float(np.float32(scale)), causal)
+    eo, el = max_abs(to_host_f64(o), ro), max_abs(to_host_f64(lse), rl)
+    say(f"    max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O[dtype], eo
+    assert el <= TOL_LSE, el
+    return o, lse
+
+
+SMALL = [
+    # (B, H, N, d) : several tiles, ragged tails, single row, XCD-grouped head counts
+    (1, 2, 1, 64), (1, 2, 17, 128), (1, 3, 100, 64), (2, 4, 255, 128), (1, 2, 256, 64),
+    (1, 1, 300, 128), (2, 4, 513, 64), (1, 2, 1000, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes_all_elements(gpu, shape, causal, dtype):
+    B, H, N, d = shape
+    say(f"[fwd small] B={B} H={H} N={N} d={d} causal={causal} {dtype}")
+    qb, kb, vb = fa_inputs.qkv_bits(B, H, N, d, dtype, seed=1000 + N + d)
+    check_full(qb, kb, vb, dtype, causal, gpu)
+
+
+def test_config_c1_all_elements(gpu):
+    c = fa_inputs.CONFIGS["c1_fwd_n256_d64_f16"]
+    say(f"[fwd c1] {c}")
+    qb, kb, vb = fa_inputs.qkv_bits(c["B"], c["H"], c["N"], c["d"], c["dtype"], c["seed"])
+    check_full(qb, kb, vb, c["dtype"], c["causal"], gpu)
+
+
+FULL = ["c2_fwd_n4096_d128_bf16", "c3_fwd_causal_n8192_d128_bf16", "c4_causal_n1024_d128_f16",
+        "c4_causal_n4096_d128_f16", "c4_causal_n16384_d128_f16", "c4_causal_n32768_d128_f16",
+        "c4_causal_n16384_d64_f16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(gpu, name):
+    c = fa_inputs.CONFIGS[name]
+    B, H, N, d, dtype, causal = c["B"], c["H"], c["N"], c["d"], c["dtype"], c["causal"]
+    say(f"[fwd full] {name}")
+    qb, kb, vb = fa_inputs.qkv_bits(B, H, N, d, dtype, c["seed"])
+    o, lse = run_fwd(qb, kb, vb, dtype, causal, gpu)
+    o_h, lse_h = to_host_f64(o), to_host_f64(lse)
+    assert np.isfinite(o_h).all() and np.isfinite(lse_h).all()
+    plan = fa.fa_fwd_plan(B, H, N, d, causal, 1 if dtype == "bf16" else 0)
+    heads = sorted({0, B * H - 1, (B * H) // 2})
+    rows = sample_rows(N, plan.block_m, 96, seed=N)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    worst_o = worst_l = 0.0
+    for bh in heads:
+        b, h = divmod(bh, H)
+        sub = [fa_inputs.widen(x[b:b + 1, h:h + 1], dtype) for x in (qb, kb, vb)]
+        ro, rl = oracle.fwd_rows(*sub, scale, causal, rows)
+        worst_o = max(worst_o, max_abs(o_h[b, h, rows], ro))
+        worst_l = max(worst_l, max_abs(lse_h[b, h, rows], rl))
+    say(f"    {len(heads)} heads x {len(rows)} rows: max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+    assert worst_o <= TOL_O[dtype]
+    assert worst_l <= TOL_LSE
+
+
+# ---- closed forms through the GPU path -------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_values(gpu, causal, dtype):
+    B, H, N, d = 1, 2, 300, 128
+    qb, _, vb = fa_inputs.qkv_bits(B, H, N, d, dtype, seed=77)
+    kb = np.broadcast_to(fa_inputs.normal_bits(H * d, dtype, 78, 1).reshape(1, H, 1, d), (B, H, N, d)).copy()
+    o, lse = run_fwd(qb, kb, vb, dtype, causal, gpu)
+    v = fa_inputs.widen(vb, dtype)
+    ref = np.cumsum(v, axis=2) / np.arange(1, N + 1)[:, None] if causal else np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+    assert max_abs(to_host_f64(o), ref) <= TOL_O[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_single_key_returns_v_exactly(gpu, d, dtype):
+    qb, kb, vb = fa_inputs.qkv_bits(2, 4, 1, d, dtype, seed=79)
+    o, lse = run_fwd(qb, kb, vb, dtype, False, gpu)
+    assert np.array_equal(to_host_f64(o), fa_inputs.widen(vb, dtype))
+    q, k = fa_inputs.widen(qb, dtype), fa_inputs.widen(kb, dtype)
+    s = (q * k).sum(-1)[..., 0] * np.float32(1 / math.sqrt(d))
+    assert max_abs(to_host_f64(lse)[..., 0], s) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_causal_row0_is_v0_exactly(gpu, dtype):
+    qb, kb, vb = fa_inputs.qkv_bits(2, 4, 777, 128, dtype, seed=80)
+    o, _ = run_fwd(qb, kb, vb, dtype, True, gpu)
+    assert np.array_equal(to_host_f64(o)[:, :, 0], fa_inputs.widen(vb, dtype)[:, :, 0])
+
+
+def test_large_scores_stay_finite(gpu):
+    # scores of magnitude ~100: the running max keeps exp2 in range
+    B, H, N, d = 1, 2, 512, 64
+    qb, kb, vb = fa_inputs.qkv_bits(B, H, N, d, "f16", seed=81)
+    q = fa_inputs.narrow(fa_inputs.widen(qb, "f16") * 8, "f16")
+    k = fa_inputs.narrow(fa_inputs.widen(kb, "f16") * 8, "f16")
+    check_full(q, k, vb, "f16", False, gpu)
+
+
+def test_forward_is_bitwise_repeatable(gpu):
+    qb, kb, vb = fa_inputs.qkv_bits(2, 8, 2048, 128, "bf16", seed=82)
+    o1, l1 = run_fwd(qb, kb, vb, "bf16", True, gpu)
+    o2, l2 = run_fwd(qb, kb, vb, "bf16", True, gpu)
+    import torch
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_misaligned_pointer_is_rejected(gpu):
+    import torch
+    x = torch.zeros(1 * 1 * 16 * 64 + 8, dtype=torch.float16, device=gpu)
+    view = x[1:1 + 16 * 64].view(1, 1, 16, 64)  # 2-byte offset
+    lse = torch.empty(1, 1, 16, device=gpu)
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd(view, view, view, view, lse, 0.125, False)
+    assert e.value.status == 5
