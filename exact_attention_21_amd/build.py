@@ -33,7 +33,10 @@ def compile_flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
             # no packed fp32 VALU instructions in device code
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # the kernels never rely on NaN semantics (masks use -inf), so max/min
+            # need no NaN canonicalisation; MFMA accumulators live in arch VGPRs
+            "-fno-honor-nans", "-mllvm", "--amdgpu-mfma-vgpr-form"]
 
 
 def build(verbose: bool = False) -> str:

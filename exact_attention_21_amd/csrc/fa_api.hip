@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "fa.h"
 #include "fa_kernels.h"
@@ -43,11 +44,9 @@ int check_common(int B, int H, int N, int d, int causal, int dtype) {
   return FA_OK;
 }
 
-// Query rows per forward workgroup = 128 * qb.
-int fwd_qb(int N, int d) {
-  (void)d;
-  return N > 128 ? 2 : 1;
-}
+// Query rows per forward workgroup = 128 * qb.  d = 128 uses 32 rows per wave
+// (register budget); d = 64 uses 64 rows per wave once N is large enough.
+int fwd_qb(int N, int d) { return d == 128 ? FWD_QB_D128 : (N > 128 ? 2 : 1); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -77,7 +76,7 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *pl
   if (rc) return rc;
   const int qb = fwd_qb(N, d);
   const int bm = 128 * qb;
-  const int bn = d == 128 ? fa::FWD_BN_D128 : fa::FWD_BN_D64;
+  const int bn = fa::FWD_BN;
   const long long nq = (N + bm - 1) / bm;
   const long long grid = nq * B * H;
   if (grid > 0x7fffffffLL) return FA_ERR_SHAPE;
@@ -85,7 +84,7 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *pl
   plan->block_n = bn;
   plan->threads = 256;
   plan->grid = (int)grid;
-  plan->lds_bytes = 2 * bn * ((d * 2 + 16) + (d * 2 + 64));
+  plan->lds_bytes = 2 * 2 * bn * d * 2;  // K and V rings of two tiles
   plan->xcd_grouped = ((long long)B * H) % 8 == 0;
   return FA_OK;
 }
@@ -139,25 +138,111 @@ int fa_bwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *pl
   return FA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the backward entry points; fills the parameter block's
+// shape fields and workspace pointers.
+int bwd_setup(int B, int H, int N, int d, float scale, int causal, int dtype, void *workspace,
+              size_t workspace_bytes, fa::BwdParams *p, fa_plan_t *plan) {
+  int rc = fa_bwd_plan(B, H, N, d, causal, dtype, plan);
+  if (rc) return rc;
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  if (!workspace) return FA_ERR_NULL;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_WORKSPACE;
+  const size_t rows = (size_t)B * H * N;
+  char *ws = static_cast<char *>(workspace);
+  std::memset(p, 0, sizeof *p);
+  p->dq_acc = reinterpret_cast<float *>(ws);
+  p->dws = reinterpret_cast<float *>(ws + align256(rows * d * sizeof(float)));
+  p->N = N;
+  p->n_ktiles = (N + fa::BWD_BN - 1) / fa::BWD_BN;
+  p->xcd_grouped = plan->xcd_grouped;
+  p->scale = scale;
+  p->scale_log2 = scale * 1.4426950408889634f;
+  return FA_OK;
+}
+
+bool all_aligned(std::initializer_list<const void *> ptrs) {
+  for (const void *ptr : ptrs)
+    if (!aligned16(ptr)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_preprocess(const void *o, const void *dout, int B, int H, int N, int d, int dtype,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (!o || !dout || !workspace) return FA_ERR_NULL;
+  fa::BwdParams p;
+  fa_plan_t plan;
+  int rc = bwd_setup(B, H, N, d, 1.f, 0, dtype, workspace, workspace_bytes, &p, &plan);
+  if (rc) return rc;
+  if (!all_aligned({o, dout})) return FA_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  p.o = o;
+  p.dout = dout;
+  const hipError_t e = fa::launch_bwd_pre(p, dtype, d, (long)B * H * N,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_bwd_main(const void *q, const void *k, const void *v, const void *dout, const float *lse,
+                void *dk, void *dv, int B, int H, int N, int d, float scale, int causal,
+                int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !dout || !lse || !dk || !dv || !workspace) return FA_ERR_NULL;
+  fa::BwdParams p;
+  fa_plan_t plan;
+  int rc = bwd_setup(B, H, N, d, scale, causal, dtype, workspace, workspace_bytes, &p, &plan);
+  if (rc) return rc;
+  if (!all_aligned({q, k, v, dout, lse, dk, dv})) return FA_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dout = dout;
+  p.lse = lse;
+  p.dk = dk;
+  p.dv = dv;
+  const hipError_t e = fa::launch_bwd_main(p, dtype, d, causal, plan.grid,
+                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_bwd_dq_convert(void *dq, int B, int H, int N, int d, float scale, int dtype,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (!dq || !workspace) return FA_ERR_NULL;
+  fa::BwdParams p;
+  fa_plan_t plan;
+  int rc = bwd_setup(B, H, N, d, scale, 0, dtype, workspace, workspace_bytes, &p, &plan);
+  if (rc) return rc;
+  if (!aligned16(dq)) return FA_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  p.dq = dq;
+  const hipError_t e = fa::launch_bwd_dq(p, dtype, (long)B * H * N * d,
+                                         reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
            const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
            float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
            void *stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  fa::BwdParams p;
   fa_plan_t plan;
-  int rc = fa_bwd_plan(B, H, N, d, causal, dtype, &plan);
+  int rc = bwd_setup(B, H, N, d, scale, causal, dtype, workspace, workspace_bytes, &p, &plan);
   if (rc) return rc;
-  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
-  const void *ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
-  for (const void *ptr : ptrs)
-    if (!aligned16(ptr)) return FA_ERR_ALIGN;
-  const size_t need = fa_bwd_workspace_size(B, H, N, d);
-  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!all_aligned({q, k, v, o, dout, lse, dq, dk, dv})) return FA_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
-  const size_t rows = (size_t)B * H * N;
-  char *ws = static_cast<char *>(workspace);
-  fa::BwdParams p;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -167,15 +252,11 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.dq_acc = reinterpret_cast<float *>(ws);
-  p.dws = reinterpret_cast<float *>(ws + align256(rows * d * sizeof(float)));
-  p.N = N;
-  p.n_ktiles = (N + fa::BWD_BN - 1) / fa::BWD_BN;
-  p.xcd_grouped = plan.xcd_grouped;
-  p.scale = scale;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  const hipError_t e = fa::launch_bwd(p, dtype, d, causal, plan.grid, (long)rows,
-                                      reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const long rows = (long)B * H * N;
+  hipError_t e = fa::launch_bwd_pre(p, dtype, d, rows, st);
+  if (e == hipSuccess) e = fa::launch_bwd_main(p, dtype, d, causal, plan.grid, st);
+  if (e == hipSuccess) e = fa::launch_bwd_dq(p, dtype, rows * d, st);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

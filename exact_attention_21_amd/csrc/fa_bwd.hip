@@ -363,36 +363,45 @@ void bwd_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 
 template <class T, int D>
-static hipError_t launch_bwd_t(const BwdParams &p, int causal, int grid, long rows,
-                               hipStream_t st) {
-  const int pre_grid = (int)((rows + 15) / 16);
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st,
+static hipError_t launch_pre_t(const BwdParams &p, long rows, hipStream_t st) {
+  const int grid = (int)((rows + 15) / 16);
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(grid), dim3(256), 0, st,
                      reinterpret_cast<const uint16_t *>(p.o),
                      reinterpret_cast<const uint16_t *>(p.dout), p.dws, p.dq_acc, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_main_t(const BwdParams &p, int causal, int grid, hipStream_t st) {
   if (causal)
     hipLaunchKernelGGL((bwd_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((bwd_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long n4 = rows * D / 4;
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_dq_t(const BwdParams &p, long elems, hipStream_t st) {
+  const long n4 = elems / 4;
   hipLaunchKernelGGL((bwd_dq_kernel<T>), dim3((int)((n4 + 255) / 256)), dim3(256), 0, st,
                      p.dq_acc, reinterpret_cast<uint16_t *>(p.dq), p.scale, n4);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams &p, int dtype, int d, int causal, int grid, long rows,
-                      hipStream_t st) {
-  if (dtype == 1) {
-    if (d == 128) return launch_bwd_t<BF16, 128>(p, causal, grid, rows, st);
-    if (d == 64) return launch_bwd_t<BF16, 64>(p, causal, grid, rows, st);
-  } else {
-    if (d == 128) return launch_bwd_t<F16, 128>(p, causal, grid, rows, st);
-    if (d == 64) return launch_bwd_t<F16, 64>(p, causal, grid, rows, st);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_bwd_pre(const BwdParams &p, int dtype, int d, long rows, hipStream_t st) {
+  if (dtype == 1) return d == 128 ? launch_pre_t<BF16, 128>(p, rows, st) : launch_pre_t<BF16, 64>(p, rows, st);
+  return d == 128 ? launch_pre_t<F16, 128>(p, rows, st) : launch_pre_t<F16, 64>(p, rows, st);
+}
+
+hipError_t launch_bwd_main(const BwdParams &p, int dtype, int d, int causal, int grid,
+                           hipStream_t st) {
+  if (dtype == 1)
+    return d == 128 ? launch_main_t<BF16, 128>(p, causal, grid, st) : launch_main_t<BF16, 64>(p, causal, grid, st);
+  return d == 128 ? launch_main_t<F16, 128>(p, causal, grid, st) : launch_main_t<F16, 64>(p, causal, grid, st);
+}
+
+hipError_t launch_bwd_dq(const BwdParams &p, int dtype, long elems, hipStream_t st) {
+  return dtype == 1 ? launch_dq_t<BF16>(p, elems, st) : launch_dq_t<F16>(p, elems, st);
 }
 
 }  // namespace fa

@@ -104,6 +104,38 @@ __device__ __forceinline__ u32x4 gload16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Raw buffer resource over `bytes` bytes at `base`; loads past the end return 0
+// (hardware range check), so ragged tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane i of the wave writes
+// lds_block + 16 i (the block address must be wave-uniform).  Offsets past the
+// resource's end write zeros.  Completion is tracked by vmcnt only.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds_block, uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_block, 16, byte_off, 0, 0, 0);
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt, lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without the memory fences of __syncthreads (which would
+// also drain every outstanding global load); the memory clobber keeps the
+// compiler from moving LDS accesses across it.  Callers wait for the LDS
+// traffic that must be visible before calling it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }   // v_log_f32 (base 2)
 

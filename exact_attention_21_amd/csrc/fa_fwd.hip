@@ -1,50 +1,101 @@
 // Fused attention forward for gfx950.
 //
-// One workgroup = 4 waves = BM = 4 * 32 * QB query rows of one (batch, head);
-// each wave owns 32 * QB rows.  The workgroup streams K/V tiles of BN keys
-// through double-buffered LDS and runs the online softmax of the MHA tuning
-// handbook ch.3 ("core idea": running max and running sum; "engineering
-// implementation": per-block max, rescaling of the old partial output and sum,
-// LSE kept per row).  Normalisation by the row sum happens once, in the
-// epilogue, which is algebraically the same as the per-block division of that
-// pseudocode.  Work partition follows the FA1-vs-FA2 page (section 2.1: each
-// workgroup handles one query block, query fragments held in registers, K/V
-// shared through on-chip memory; section 2.2: the next K/V tile is prefetched
-// while the current one is computed).
+// One workgroup = 4 waves = BM = 128 * QB query rows of one (batch, head); each
+// wave owns 32 * QB rows.  The workgroup streams K/V tiles of BN = 32 keys
+// through LDS and runs the online softmax of the MHA tuning handbook ch.3
+// ("core idea": running max and running sum; "engineering implementation":
+// per-block max, rescaling of the old partial output and sum, LSE kept per
+// row).  Normalisation by the row sum happens once, in the epilogue, which is
+// algebraically the same as that pseudocode's per-block division.  Work
+// partition follows the FA1-vs-FA2 page (section 2.1: each workgroup handles one
+// query block with its query fragments held in registers and K/V shared
+// through on-chip memory; section 2.2: later K/V tiles are fetched while the
+// current one is computed).
 //
-// Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMAs: the A
-// operand is a K fragment read from LDS, the B operand a Q fragment held in
-// registers for the whole loop.  In the S^T accumulator a lane owns one query
-// (l % 32) and 16 keys, so a row max/sum needs only in-lane reductions plus one
-// exchange with the other half-wave.  The same registers, packed to 16 bits,
-// are directly the B operand of O^T += V^T P^T; the V^T operand comes from LDS
-// with the transposing read ds_read_b64_tr_b16.  Exponentials are base 2 with
-// log2(e) folded into the score scale.
+// Scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMAs: the A operand
+// is a K fragment read from LDS, the B operand a Q fragment held in registers
+// for the whole loop.  In the S^T accumulator a lane owns one query (l % 32)
+// and 16 keys, so a row max/sum needs in-lane reductions plus one exchange with
+// the other half-wave.  The same registers, packed to 16 bits, are directly the
+// B operand of O^T += V^T P^T; the V^T operand comes from LDS through the
+// transposing read ds_read_b64_tr_b16.  Exponentials are base 2 with log2(e)
+// folded into the score scale.
+//
+// K/V tiles reach LDS by direct buffer->LDS loads (no staging registers) one
+// step ahead, into rings of two slots.  Tiles are stored with unpadded rows and
+// an XOR swizzle of the 16-byte chunk index chosen per access pattern (K: chunk
+// ^ (row & 15), conflict-free for the 16-byte fragment reads; V: chunk ^ ((row
+// & 3) << 1), conflict-free for the transposing reads).  Rows past the end of
+// the sequence load as zeros (hardware range check).
+//
+// Latency is hidden by occupancy rather than by software pipelining: the kernel
+// fits in 168 VGPRs, so three workgroups (12 waves) share a CU and the
+// sequencer interleaves one wave's exponentials with another's MFMAs.  Each
+// row's running max is raised lazily: only when the row's max grows by more
+// than 2^8 are its running max, row sum and output row rescaled (the output
+// rescale is a wave-uniform, rarely taken branch).  Between raises the
+// exponentials are taken against a stale max, so p <= 2^8; the final
+// normalisation uses the same stale max in numerator and denominator, so the
+// result is unchanged.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 
-template <class T, int D, int QB, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+namespace {
+
+constexpr float LAZY_TAU = 8.0f;  // log2 growth of a row max that forces a rescale
+constexpr int PREFETCH = 1;       // steps between issuing a tile's load and its use
+constexpr int NSLOT = PREFETCH + 1;
+
+// o *= a for an accumulator that lives in AGPRs (rare path): read, scale and
+// write back each register without moving the accumulator out of AGPRs.
+__device__ __forceinline__ void scale_acc_agpr(f32x16 &acc, float a) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = acc[i], tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(a));
+    acc[i] = x;
+  }
+}
+
+// XOR swizzles of the 16-byte chunk index within a tile row.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return ((row & 3) << 1) & (D / 8 - 1);
+}
+
+}  // namespace
+
+template <class T, int D, int QB, bool CAUSAL, bool O_IN_AGPR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_SIMD, FWD_WAVES_PER_SIMD)))
 void fwd_kernel(FwdParams p) {
+  constexpr int BN = FWD_BN;
   constexpr int BM = 128 * QB;          // query rows per workgroup
   constexpr int WR = 32 * QB;           // query rows per wave
-  constexpr int KS = D * 2 + 16;        // LDS row stride of K tiles (bytes)
-  constexpr int VS = D * 2 + 64;        // LDS row stride of V tiles (bytes)
-  constexpr int KT = BN * KS;           // bytes of one K tile
-  constexpr int VT = BN * VS;           // bytes of one V tile
-  constexpr int STAGE = KT + VT;
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int CPT = BN * CPR / 256;   // chunks per thread per tile (K or V)
-  constexpr int ND16 = D / 16, ND32 = D / 32, NK32 = BN / 32, NK16 = BN / 16;
-  static_assert(BN * CPR % 256 == 0, "tile must split evenly over 256 threads");
+  constexpr int RB = D * 2;             // bytes per tile row (unpadded)
+  constexpr int TB = BN * RB;           // bytes of one K (or V) tile
+  constexpr int OFF_V = NSLOT * TB;     // K ring, then V ring
+  constexpr int CPR = RB / 16;          // 16-byte chunks per row
+  constexpr int ROWS_PER_BLOCK = 64 / CPR;       // rows covered by one 1 KB DMA block
+  constexpr int BLOCKS = TB / 1024;              // DMA blocks per tile
+  constexpr int BPW = BLOCKS / 4;                // DMA blocks per wave per tile
+  constexpr int DMA_PER_STEP = 2 * BPW;          // K + V loads issued per wave per step
+  constexpr int ND16 = D / 16, ND32 = D / 32;
+  static_assert(BLOCKS % 4 == 0, "tile must split evenly over 4 waves");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
+  const int g = lane >> 4, s16 = lane & 15;
   const int N = p.N;
 
   // ---- which (head, query tile) this workgroup computes
@@ -65,21 +116,43 @@ void fwd_kernel(FwdParams p) {
   }
   const int i0 = qt * BM;
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + hoff;
-  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + hoff;
-  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + hoff;
-
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + hoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + hoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + hoff, head_bytes);
   const int wr0 = i0 + w * WR;  // first query row of this wave
+
+  const int kend = CAUSAL ? min(N, i0 + BM) : N;
+  const int nt = (kend + BN - 1) / BN;
+  const float sl2 = p.scale_log2;
+
+  // ---- K/V tile DMA: this lane's share of block (w * BPW + j) of a tile
+  uint32_t dma_k_off[BPW], dma_v_off[BPW];  // byte offset inside a tile (swizzled source)
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int blk = w * BPW + j;
+    const int row = blk * ROWS_PER_BLOCK + lane / CPR, pos = lane % CPR;
+    dma_k_off[j] = (uint32_t)(row * RB + ((pos ^ swz_k<D>(row)) << 4));
+    dma_v_off[j] = (uint32_t)(row * RB + ((pos ^ swz_v<D>(row)) << 4));
+  }
+  auto issue_tile = [&](const __amdgpu_buffer_rsrc_t &rsrc, int t, int ring_off,
+                        const uint32_t (&offs)[BPW]) {
+    // tiles outside [0, nt) load as zeros (offset past the resource end)
+    const bool ok = t >= 0 && t < nt;
+    const uint32_t base = ok ? (uint32_t)t * TB : 0x80000000u;
+    char *slot = smem + ring_off + ((t + NSLOT) % NSLOT) * TB;
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) dma16(rsrc, slot + (w * BPW + j) * 1024, base + offs[j]);
+  };
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
   u32x4 qf[QB][ND16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = wr0 + qb * 32 + l32;
+    const int row = wr0 + qb * 32 + l32;  // rows past N read as zeros
 #pragma unroll
-    for (int db = 0; db < ND16; ++db) {
-      qf[qb][db] = row < N ? gload16(Qh + (size_t)row * D + db * 16 + hi * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int db = 0; db < ND16; ++db)
+      qf[qb][db] = bload16(rq, (uint32_t)(row * D + db * 16 + hi * 8) * 2);
   }
 
   f32x16 oacc[QB][ND32];
@@ -87,149 +160,146 @@ void fwd_kernel(FwdParams p) {
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int c = 0; c < ND32; ++c) oacc[qb][c] = f32x16{};
-  float mrow[QB], lrow[QB];  // running max (log2 units) and this lane's partial sum
+  float mrun[QB], lrun[QB];  // running max (log2 units) and this lane's partial row sum
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    mrow[qb] = -__builtin_inff();
-    lrow[qb] = 0.f;
+    mrun[qb] = -__builtin_inff();
+    lrun[qb] = 0.f;
   }
 
-  const int kend = CAUSAL ? min(N, i0 + BM) : N;
-  const int ntiles = (kend + BN - 1) / BN;
-  const float sl2 = p.scale_log2;
+  f32x16 sacc[QB];
+  uint32_t pk[QB][8];
 
-  // ---- K/V tile loading: global -> registers -> LDS (row-padded layout)
-  u32x4 pre[2 * CPT];
-  auto gfetch = [&](int t) {
-    const int j0 = t * BN;
+  // fragment-read addresses inside a slot
+  const int k_rd = l32 * RB;
+  const int k_sw = swz_k<D>(l32);
+  const int v_row = 4 * (g >> 1) + (s16 >> 2);  // + 16 kb (+ 8 for the second read)
+  const int v_sw = swz_v<D>(v_row);             // row & 3 is unchanged by +16 kb and +8
+
+  // S(t) = K(t) Q^T
+  auto stage_s = [&](int t, f32x16 (&s)[QB]) {
+    const char *ks = smem + (t % NSLOT) * TB;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + 256 * c;
-      const int row = ch / CPR, col = ch % CPR;
-      const bool ok = j0 + row < N;
-      const size_t off = (size_t)(j0 + row) * D + col * 8;
-      pre[c] = ok ? gload16(Kh + off) : u32x4{0, 0, 0, 0};
-      pre[CPT + c] = ok ? gload16(Vh + off) : u32x4{0, 0, 0, 0};
+    for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+    for (int db = 0; db < ND16; ++db) {
+      const u32x4 a = lds_read16(ks + k_rd + (((2 * db + hi) ^ k_sw) << 4));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb] = T::mma(a, qf[qb][db], s[qb]);
     }
   };
-  auto lstore = [&](int stage) {
-    char *ks = smem + stage * STAGE;
-    char *vs = ks + KT;
+  // masking of tile t: causal diagonal and the ragged key tail
+  auto needs_mask = [&](int t) {
+    const int j0 = t * BN;
+    return (CAUSAL && j0 + BN - 1 > wr0) || (j0 + BN > N);
+  };
+  auto apply_mask = [&](int t, f32x16 (&s)[QB]) {
+    const int j0 = t * BN;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + 256 * c;
-      const int row = ch / CPR, col = ch % CPR;
-      lds_write16(ks + row * KS + col * 16, pre[c]);
-      lds_write16(vs + row * VS + col * 16, pre[CPT + c]);
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = wr0 + qb * 32 + l32;
+      const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;  // last visible key
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[qb][r] = key <= lim ? s[qb][r] : -__builtin_inff();
+      }
     }
   };
-
-  gfetch(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) gfetch(t + 1);
-    const char *ks = smem + (t & 1) * STAGE;
-    const char *vs = ks + KT;
-    const int j0 = t * BN;
-    const bool active = !CAUSAL || j0 <= wr0 + WR - 1;
-    if (active) {
-      // -- S^T = K Q^T for BN keys x WR queries
-      f32x16 s[NK32][QB];
+  // softmax of one tile: new (lazy) running max, probabilities packed to 16 bits,
+  // row sums; returns whether the running max moved (output must be rescaled)
+  auto stage_softmax = [&](f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&alpha)[QB]) {
+    bool grow_any = false;
 #pragma unroll
-      for (int kb = 0; kb < NK32; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = fmaxf(s[qb][0], s[qb][1]);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+      for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][r], s[qb][r + 1]));
+      mx = max_xhalf(mx) * sl2;
+      // per-row lazy update (a lane-wise select, not a branch)
+      const bool grow = mx > mrun[qb] + LAZY_TAU;
+      const float mu = grow ? mx : mrun[qb];
+      alpha[qb] = grow ? fast_exp2(mrun[qb] - mx) : 1.f;
+      grow_any |= grow;
+      mrun[qb] = mu;
+      const float nm = -mu;
+      float ls = 0.f;
 #pragma unroll
-      for (int db = 0; db < ND16; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < NK32; ++kb) {
-          const u32x4 a = lds_read16(ks + (kb * 32 + l32) * KS + db * 32 + hi * 16);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = T::mma(a, qf[qb][db], s[kb][qb]);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const float e0 = fast_exp2(__builtin_fmaf(s[qb][2 * j], sl2, nm));
+        const float e1 = fast_exp2(__builtin_fmaf(s[qb][2 * j + 1], sl2, nm));
+        pk[qb][j] = T::pack(e0, e1);
+        ls += e0 + e1;  // row sum from the unrounded probabilities (LSE accuracy)
       }
-      // -- mask: causal diagonal tiles and the ragged tail of the keys
-      const bool need_mask = (CAUSAL && j0 + BN - 1 > wr0) || (j0 + BN > N);
-      if (need_mask) {
+      lrun[qb] = lrun[qb] * alpha[qb] + ls;
+    }
+    return grow_any;
+  };
+  // O^T += V(t)^T P(t)^T
+  auto stage_pv = [&](int t, const uint32_t (&pk)[QB][8]) {
+    const char *vs = smem + OFF_V + (t % NSLOT) * TB;
 #pragma unroll
-        for (int kb = 0; kb < NK32; ++kb)
+    for (int c = 0; c < ND32; ++c) {
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const int qrow = wr0 + qb * 32 + l32;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int byte = c * 64 + 32 * (g & 1) + 8 * (s16 & 3);
+        const char *ap = vs + (kb * 16 + v_row) * RB + (((byte >> 4) ^ v_sw) << 4) + (byte & 15);
+        const u32x2 a0 = lds_read_tr4(ap);
+        const u32x2 a1 = lds_read_tr4(ap + 8 * RB);
+        const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              const bool masked = (CAUSAL && key > qrow) || key >= N;
-              if (masked) s[kb][qb][r] = -__builtin_inff();
-            }
-          }
-      }
-      // -- online softmax: new running max, rescale factor, exponentials, row sum
-      uint32_t pk[NK16][QB][4];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int kb = 0; kb < NK32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        mx = max_xhalf(mx);
-        const float mnew = fmaxf(mrow[qb], mx * sl2);
-        const float mu = mnew == -__builtin_inff() ? 0.f : mnew;  // no (-inf) - (-inf)
-        const float alpha = fast_exp2(mrow[qb] - mu);
-        mrow[qb] = mnew;
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NK32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(__builtin_fmaf(s[kb][qb][r], sl2, -mu));
-            s[kb][qb][r] = e;
-            ls += e;
-          }
-        lrow[qb] = lrow[qb] * alpha + ls;
-#pragma unroll
-        for (int c = 0; c < ND32; ++c) oacc[qb][c] *= alpha;
-#pragma unroll
-        for (int kb = 0; kb < NK32; ++kb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              pk[kb * 2 + h][qb][j] = T::pack(s[kb][qb][8 * h + 2 * j], s[kb][qb][8 * h + 2 * j + 1]);
-      }
-      // -- O^T += V^T P^T ; V^T fragments by transposing LDS reads
-      const int g = lane >> 4, s16 = lane & 15;
-#pragma unroll
-      for (int c = 0; c < ND32; ++c) {
-#pragma unroll
-        for (int kb = 0; kb < NK16; ++kb) {
-          const int krow = kb * 16 + 4 * (g >> 1) + (s16 >> 2);
-          const int col = c * 32 + 16 * (g & 1) + 4 * (s16 & 3);
-          const char *a0p = vs + krow * VS + col * 2;
-          const u32x2 a0 = lds_read_tr4(a0p);
-          const u32x2 a1 = lds_read_tr4(a0p + 8 * VS);
-          const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const u32x4 b = {pk[kb][qb][0], pk[kb][qb][1], pk[kb][qb][2], pk[kb][qb][3]};
-            oacc[qb][c] = T::mma(a, b, oacc[qb][c]);
-          }
+        for (int qb = 0; qb < QB; ++qb) {
+          const u32x4 b = {pk[qb][4 * kb], pk[qb][4 * kb + 1], pk[qb][4 * kb + 2], pk[qb][4 * kb + 3]};
+          oacc[qb][c] = T::mma(a, b, oacc[qb][c]);
         }
       }
     }
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
-    __syncthreads();
+  };
+  auto rescale_o = [&](const float (&alpha)[QB]) {
+    if constexpr (O_IN_AGPR) {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // MFMA results settle before reads
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int c = 0; c < ND32; ++c) scale_acc_agpr(oacc[qb][c], alpha[qb]);
+      asm volatile("s_nop 4");
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int c = 0; c < ND32; ++c) oacc[qb][c] *= alpha[qb];
+    }
+  };
+
+  // K(t + PREFETCH) and V(t + PREFETCH) are issued at step t
+  auto issue_step = [&](int t) {
+    issue_tile(rk, t + PREFETCH, 0, dma_k_off);
+    issue_tile(rv, t + PREFETCH, OFF_V, dma_v_off);
+  };
+#pragma unroll
+  for (int t = -PREFETCH; t < 0; ++t) issue_step(t);
+  wait_vmcnt<DMA_PER_STEP * (PREFETCH - 1)>();
+  barrier_only();
+  for (int t = 0; t < nt; ++t) {
+    issue_step(t);
+    stage_s(t, sacc);
+    if (needs_mask(t)) apply_mask(t, sacc);
+    float alpha[QB];
+    const bool resc = stage_softmax(sacc, pk, alpha);
+    if (__builtin_amdgcn_ballot_w64(resc) != 0) rescale_o(alpha);
+    stage_pv(t, pk);
+    // tiles used at step t+1 were issued PREFETCH-1 steps ago
+    wait_vmcnt<DMA_PER_STEP * (PREFETCH - 1)>();
+    barrier_only();
   }
+  wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
   // ---- epilogue: O = acc / l (rounded to 16 bits), LSE = (m + log2 l) ln 2
   uint16_t *Oh = reinterpret_cast<uint16_t *>(p.o) + hoff;
   float *Lh = p.lse + (size_t)bh * N;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = lrow[qb] + xhalf(lrow[qb]);
+    const float lt = lrun[qb] + xhalf(lrun[qb]);
     const float inv = 1.f / lt;
     const int row = wr0 + qb * 32 + l32;
     if (row < N) {
@@ -243,7 +313,7 @@ void fwd_kernel(FwdParams p) {
           st[1] = T::pack(oacc[qb][c][4 * rg + 2] * inv, oacc[qb][c][4 * rg + 3] * inv);
           *reinterpret_cast<u32x2 *>(Oh + (size_t)row * D + dcol) = st;
         }
-      if (hi == 0) Lh[row] = (mrow[qb] + fast_log2(lt)) * 0.69314718055994531f;
+      if (hi == 0) Lh[row] = (mrun[qb] + fast_log2(lt)) * 0.69314718055994531f;
     }
   }
 }
@@ -252,29 +322,27 @@ void fwd_kernel(FwdParams p) {
 // instantiation table
 // ---------------------------------------------------------------------------
 
-template <class T, int D, int QB, int BN, bool C>
+template <class T, int D, int QB, bool C>
 static hipError_t launch_fwd_t(const FwdParams &p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<T, D, QB, BN, C>), dim3(grid), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdParams &p, int dtype, int d, int causal, int qb, int grid,
                       hipStream_t st) {
-#define FA_FWD_CASE(TT, DD, QQ, BB)                                                   \
+#define FA_FWD_CASE(TT, DD, QQ)                                                       \
   if (d == DD && qb == QQ) {                                                          \
-    return causal ? launch_fwd_t<TT, DD, QQ, BB, true>(p, grid, st)                   \
-                  : launch_fwd_t<TT, DD, QQ, BB, false>(p, grid, st);                 \
+    return causal ? launch_fwd_t<TT, DD, QQ, true>(p, grid, st)                       \
+                  : launch_fwd_t<TT, DD, QQ, false>(p, grid, st);                     \
   }
   if (dtype == 1) {
-    FA_FWD_CASE(BF16, 128, 1, FWD_BN_D128)
-    FA_FWD_CASE(BF16, 128, 2, FWD_BN_D128)
-    FA_FWD_CASE(BF16, 64, 1, FWD_BN_D64)
-    FA_FWD_CASE(BF16, 64, 2, FWD_BN_D64)
+    FA_FWD_CASE(BF16, 128, FWD_QB_D128)
+    FA_FWD_CASE(BF16, 64, 1)
+    FA_FWD_CASE(BF16, 64, 2)
   } else {
-    FA_FWD_CASE(F16, 128, 1, FWD_BN_D128)
-    FA_FWD_CASE(F16, 128, 2, FWD_BN_D128)
-    FA_FWD_CASE(F16, 64, 1, FWD_BN_D64)
-    FA_FWD_CASE(F16, 64, 2, FWD_BN_D64)
+    FA_FWD_CASE(F16, 128, FWD_QB_D128)
+    FA_FWD_CASE(F16, 64, 1)
+    FA_FWD_CASE(F16, 64, 2)
   }
 #undef FA_FWD_CASE
   return hipErrorInvalidValue;

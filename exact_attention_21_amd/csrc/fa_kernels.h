@@ -7,9 +7,21 @@
 
 namespace fa {
 
-// Keys per K/V tile of the forward kernel, by head dim.
-constexpr int FWD_BN_D128 = 64;
-constexpr int FWD_BN_D64 = 64;
+// Keys per K/V tile (one pipeline step) of the forward kernel.
+constexpr int FWD_BN = 32;
+// Query blocks of 32 rows per wave for head dim 128, and whether the output
+// accumulator is kept in AGPRs (set together with the compiler's MFMA register
+// form for fa_fwd.hip).
+#ifndef FWD_QB_D128
+#define FWD_QB_D128 1
+#endif
+#ifndef FWD_O_IN_AGPR
+#define FWD_O_IN_AGPR (FWD_QB_D128 == 2)
+#endif
+// Waves per SIMD the forward kernel is compiled for (occupancy target).
+#ifndef FWD_WAVES_PER_SIMD
+#define FWD_WAVES_PER_SIMD 3
+#endif
 
 struct FwdParams {
   const void *q, *k, *v;
@@ -38,8 +50,13 @@ struct BwdParams {
   float scale_log2;
 };
 
-hipError_t launch_bwd(const BwdParams &p, int dtype, int d, int causal, int grid, long rows,
-                      hipStream_t st);
+// D = rowsum(dO * O) and zeroed dQ accumulator (reads p.o, p.dout; writes p.dws, p.dq_acc)
+hipError_t launch_bwd_pre(const BwdParams &p, int dtype, int d, long rows, hipStream_t st);
+// main backward kernel (writes p.dk, p.dv, accumulates p.dq_acc)
+hipError_t launch_bwd_main(const BwdParams &p, int dtype, int d, int causal, int grid,
+                           hipStream_t st);
+// dQ = scale * accumulator -> 16 bits (reads p.dq_acc, writes p.dq)
+hipError_t launch_bwd_dq(const BwdParams &p, int dtype, long elems, hipStream_t st);
 
 hipError_t launch_fwd(const FwdParams &p, int dtype, int d, int causal, int qb, int grid,
                       hipStream_t st);

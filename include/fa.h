@@ -97,6 +97,28 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The three stages fa_bwd runs, in order, on one stream; exposed so that a
+ * caller can schedule or time them separately.  They share fa_bwd's argument
+ * rules and workspace layout; fa_bwd(...) is exactly
+ *   fa_bwd_preprocess -> fa_bwd_main -> fa_bwd_dq_convert.
+ *
+ * fa_bwd_preprocess: reads o and dout; writes D_i = sum_c dO_ic O_ic (fp32) into
+ *   the workspace and zeroes its fp32 dQ accumulator.
+ * fa_bwd_main: recomputes P from q, k and lse (scale and causal as in the
+ *   forward), writes dk and dv, and adds dS K into the workspace's dQ
+ *   accumulator with fp32 atomics.  Needs fa_bwd_preprocess's workspace.
+ * fa_bwd_dq_convert: writes dq = scale * accumulator, rounded to `dtype`.
+ */
+int fa_bwd_preprocess(const void *o, const void *dout, int B, int H, int N, int d,
+                      int dtype, void *workspace, size_t workspace_bytes, void *stream);
+int fa_bwd_main(const void *q, const void *k, const void *v, const void *dout,
+                const float *lse, void *dk, void *dv, int B, int H, int N, int d,
+                float scale, int causal, int dtype, void *workspace,
+                size_t workspace_bytes, void *stream);
+int fa_bwd_dq_convert(void *dq, int B, int H, int N, int d, float scale, int dtype,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Launch plan of a forward call (host-only, no GPU needed). */
 typedef struct {
   int block_m;          /* query rows per workgroup */

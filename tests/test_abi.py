@@ -35,7 +35,7 @@ def test_status_strings():
 @pytest.mark.parametrize("N,d,causal", [(256, 64, 0), (4096, 128, 0), (8192, 128, 1), (1, 128, 1), (1000, 64, 1)])
 def test_forward_plan(N, d, causal):
     p = fa.fa_fwd_plan(4, 32, N, d, causal, fa.FA_BF16)
-    assert p.threads == 256 and p.block_m in (128, 256) and p.block_n in (64, 128)
+    assert p.threads == 256 and p.block_m in (128, 256) and p.block_n in (32, 64, 128)
     assert p.grid == -(-N // p.block_m) * 4 * 32
     assert p.lds_bytes <= 160 * 1024
     assert p.xcd_grouped == 1
