@@ -2,7 +2,7 @@
 """Attention throughput on one MI355X: fused forward + recompute backward.
 
 One step = one pass of the whole hot path over one batch: fa_fwd (O, LSE) then
-fa_bwd (D = rowsum(dO*O), the main backward kernel, dQ conversion) on the
+the backward's three stages (D = rowsum(dO*O), the dK/dV pass, the dQ pass) on the
 causal workload B=4, H=32, N=8192, d=128, bf16, with Q, K, V, dO i.i.d. N(0,1)
 from a fixed seed, all resident in HBM before timing starts.
 
@@ -134,23 +134,27 @@ def main():
     scale = 1 / math.sqrt(d)
     stream = torch.cuda.current_stream()
 
+    # one step: forward, then the three backward stages; events bracket each
+    # kernel on the stream it runs on
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
         fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
-        if ev is not None:
-            ev[1].record(stream)
+        rec(1)
         if not args.fwd_only:
-            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, ws, stream)
-            if ev is not None:
-                ev[2].record(stream)
+            fa.fa_bwd_preprocess(o, do, lse, ws, stream)
+            rec(2)
+            fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, causal, ws, stream)
+            rec(3)
+            fa.fa_bwd_dq(q, k, v, do, dq, scale, causal, ws, stream)
+            rec(4)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -159,22 +163,38 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs] if not args.fwd_only else [0.0]
+    def avg_ms(i, j):
+        return sum(e[i].elapsed_time(e[j]) for e in evs) / len(evs)
+
     f_fwd, f_bwd = nominal_flop(B, H, N, d, causal)
     ms_step = wall * 1e3 / args.steps
-    fwd_avg = sum(fwd_ms) / len(fwd_ms)
-    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    kern = {"fwd_kernel": (avg_ms(0, 1), f_fwd)}
+    if not args.fwd_only:
+        # algorithmic FLOP of each backward pass: dK/dV runs 4 of the tile
+        # products (S, dP, dV, dK), dQ runs 3 (S, dP, dQ); each is 2 B H N^2 d
+        # (halved when causal), i.e. half the nominal forward's 4 B H N^2 d
+        kern["bwd_pre_kernel"] = (avg_ms(1, 2), 0.0)
+        kern["bwd_dkdv_kernel"] = (avg_ms(2, 3), 2.0 * f_fwd)
+        kern["bwd_dq_kernel"] = (avg_ms(3, 4), 1.5 * f_fwd)
+    fwd_avg = kern["fwd_kernel"][0]
+    bwd_avg = avg_ms(1, 4) if not args.fwd_only else 0.0
     total_flop = f_fwd + (0 if args.fwd_only else f_bwd)
     fwd_tf = f_fwd / (fwd_avg * 1e-3) / 1e12
     bwd_tf = f_bwd / (bwd_avg * 1e-3) / 1e12 if not args.fwd_only else None
+    for name, (ms, fl) in kern.items():
+        log(f"[bench] {name}: {ms:.3f} ms" + (f" ({fl / (ms * 1e-3) / 1e12:.0f} TFLOP/s)" if fl else ""))
     log(f"[bench] fwd {fwd_avg:.3f} ms ({fwd_tf:.0f} TFLOP/s)"
-        + ("" if args.fwd_only else f"  bwd {bwd_avg:.3f} ms ({bwd_tf:.0f} TFLOP/s)"))
+        + ("" if args.fwd_only else f"  bwd {bwd_avg:.3f} ms ({bwd_tf:.0f} TFLOP/s nominal)"))
 
-    roofline = {"kernel": "fwd_kernel (fa_fwd, one launch per step)", "bound": "mfma",
-                "achieved": fwd_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": fwd_tf / PEAK_BF16_TFLOPS, "traffic": None,
-                "avg_launch_ms": fwd_avg, "algorithmic_flop_per_launch": f_fwd}
+    dom = max(kern, key=lambda n: kern[n][0])
+    dom_ms, dom_flop = kern[dom]
+    dom_tf = dom_flop / (dom_ms * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": dom_tf, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": dom_tf / PEAK_BF16_TFLOPS, "traffic": None,
+                "avg_launch_ms": dom_ms, "algorithmic_flop_per_launch": dom_flop}
+    kernels = {n: {"avg_ms": ms, "tflops": (fl / (ms * 1e-3) / 1e12) if fl else None,
+                   "frac_of_peak": (fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if fl else None}
+               for n, (ms, fl) in kern.items()}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -201,6 +221,7 @@ def main():
         "fwd_tflops": fwd_tf, "bwd_tflops": bwd_tf,
         "fwd_frac_of_peak": fwd_tf / PEAK_BF16_TFLOPS,
         "bwd_frac_of_peak": (bwd_tf / PEAK_BF16_TFLOPS) if bwd_tf else None,
+        "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -7,7 +7,7 @@ the library's kernels.  There is no fallback: if libfa.so is missing or the
 device is not gfx950 the calls raise.
 
 Names mirror the C ABI: fa_fwd, fa_bwd (and its three stages fa_bwd_preprocess,
-fa_bwd_main, fa_bwd_dq_convert), fa_bwd_workspace_size, fa_fwd_plan, fa_bwd_plan,
+fa_bwd_dkdv, fa_bwd_dq), fa_bwd_workspace_size, fa_fwd_plan, fa_bwd_plan,
 fa_status_str.  fwd() and bwd() are conveniences that allocate the
 outputs (and the backward workspace) with torch and call fa_fwd / fa_bwd.
 """
@@ -47,12 +47,12 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.restype = I
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp, Z, vp]
         L.fa_bwd.restype = I
-        L.fa_bwd_preprocess.argtypes = [vp, vp, I, I, I, I, I, vp, Z, vp]
+        L.fa_bwd_preprocess.argtypes = [vp, vp, vp, I, I, I, I, I, vp, Z, vp]
         L.fa_bwd_preprocess.restype = I
-        L.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp, Z, vp]
-        L.fa_bwd_main.restype = I
-        L.fa_bwd_dq_convert.argtypes = [vp, I, I, I, I, F, I, vp, Z, vp]
-        L.fa_bwd_dq_convert.restype = I
+        L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp, Z, vp]
+        L.fa_bwd_dkdv.restype = I
+        L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp, Z, vp]
+        L.fa_bwd_dq.restype = I
         L.fa_bwd_workspace_size.argtypes = [I, I, I, I]
         L.fa_bwd_workspace_size.restype = Z
         L.fa_fwd_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(fa_plan_t)]
@@ -164,42 +164,43 @@ def _ws(workspace, q):
     return _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size())
 
 
-def fa_bwd_preprocess(o, dout, workspace, stream=None) -> None:
-    """Stage 1 of fa_bwd: D = rowsum(dO * O) and a zeroed dQ accumulator in workspace."""
+def fa_bwd_preprocess(o, dout, lse, workspace, stream=None) -> None:
+    """Stage 1 of fa_bwd: D = rowsum(dO * O) and LSE * log2(e) into the workspace."""
+    import torch
     B, H, N, d = o.shape
     _check_qkv_like("dout", dout, o)
     if not o.is_contiguous():
         raise ValueError("o must be contiguous [B, H, N, d]")
-    rc = lib().fa_bwd_preprocess(_ptr(o), _ptr(dout), B, H, N, d, _dtype_code(o), *_ws(workspace, o),
-                                 _stream(stream))
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    rc = lib().fa_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(lse), B, H, N, d, _dtype_code(o),
+                                 *_ws(workspace, o), _stream(stream))
     if rc:
         raise FaError("fa_bwd_preprocess", rc)
 
 
-def fa_bwd_main(q, k, v, dout, lse, dk, dv, scale: float, causal: bool, workspace, stream=None) -> None:
-    """Stage 2 of fa_bwd: dK, dV and the fp32 dQ accumulator."""
-    import torch
+def fa_bwd_dkdv(q, k, v, dout, dk, dv, scale: float, causal: bool, workspace, stream=None) -> None:
+    """Stage 2 of fa_bwd: dK and dV (needs the preprocessed workspace)."""
     B, H, N, d = q.shape
     for name, t in (("k", k), ("v", v), ("dout", dout), ("dk", dk), ("dv", dv)):
         _check_qkv_like(name, t, q)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
-    rc = lib().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dk), _ptr(dv),
-                           B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
-                           *_ws(workspace, q), _stream(stream))
+    rc = lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dk), _ptr(dv), B, H, N, d,
+                           float(scale), int(bool(causal)), _dtype_code(q), *_ws(workspace, q),
+                           _stream(stream))
     if rc:
-        raise FaError("fa_bwd_main", rc)
+        raise FaError("fa_bwd_dkdv", rc)
 
 
-def fa_bwd_dq_convert(dq, scale: float, workspace, stream=None) -> None:
-    """Stage 3 of fa_bwd: dQ = scale * accumulator, rounded to dq's dtype."""
-    B, H, N, d = dq.shape
-    if not dq.is_contiguous():
-        raise ValueError("dq must be contiguous [B, H, N, d]")
-    rc = lib().fa_bwd_dq_convert(_ptr(dq), B, H, N, d, float(scale), _dtype_code(dq),
-                                 *_ws(workspace, dq), _stream(stream))
+def fa_bwd_dq(q, k, v, dout, dq, scale: float, causal: bool, workspace, stream=None) -> None:
+    """Stage 3 of fa_bwd: dQ (needs the preprocessed workspace)."""
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("dout", dout), ("dq", dq)):
+        _check_qkv_like(name, t, q)
+    rc = lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), B, H, N, d,
+                         float(scale), int(bool(causal)), _dtype_code(q), *_ws(workspace, q),
+                         _stream(stream))
     if rc:
-        raise FaError("fa_bwd_dq_convert", rc)
+        raise FaError("fa_bwd_dq", rc)
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None):

@@ -118,22 +118,22 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (check_common(B, H, N, d, 0, FA_BF16) != FA_OK) return 0;
   const size_t rows = (size_t)B * H * N;
-  return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+  return 2 * align256(rows * sizeof(float));
 }
 
 int fa_bwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *plan) {
   if (!plan) return FA_ERR_NULL;
   const int rc = check_common(B, H, N, d, causal, dtype);
   if (rc) return rc;
-  const long long nk = (N + fa::BWD_BN - 1) / fa::BWD_BN;
-  const long long grid = nk * B * H;
+  const long long nk = (N + fa::BWD_DKDV_BN - 1) / fa::BWD_DKDV_BN;
+  const long long nq = (N + fa::BWD_DQ_BM - 1) / fa::BWD_DQ_BM;
+  const long long grid = (nk > nq ? nk : nq) * B * H;
   if (grid > 0x7fffffffLL) return FA_ERR_SHAPE;
-  plan->block_m = fa::BWD_BM;
-  plan->block_n = fa::BWD_BN;
+  plan->block_m = fa::BWD_DKDV_BM;
+  plan->block_n = fa::BWD_DKDV_BN;
   plan->threads = 256;
-  plan->grid = (int)grid;
-  const int qs = d * 2 + 16, stage = 2 * fa::BWD_BM * qs + 2 * fa::BWD_BM * 4;
-  plan->lds_bytes = 2 * stage + fa::BWD_BN * (d * 2 + 64) + fa::BWD_BN * (fa::BWD_BM * 2 + 64);
+  plan->grid = (int)(nk * B * H);
+  plan->lds_bytes = 2 * (2 * fa::BWD_DKDV_BM * d * 2 + 512);
   plan->xcd_grouped = ((long long)B * H) % 8 == 0;
   return FA_OK;
 }
@@ -155,10 +155,11 @@ int bwd_setup(int B, int H, int N, int d, float scale, int causal, int dtype, vo
   const size_t rows = (size_t)B * H * N;
   char *ws = static_cast<char *>(workspace);
   std::memset(p, 0, sizeof *p);
-  p->dq_acc = reinterpret_cast<float *>(ws);
-  p->dws = reinterpret_cast<float *>(ws + align256(rows * d * sizeof(float)));
+  p->dws = reinterpret_cast<float *>(ws);
+  p->lse2 = reinterpret_cast<float *>(ws + align256(rows * sizeof(float)));
   p->N = N;
-  p->n_ktiles = (N + fa::BWD_BN - 1) / fa::BWD_BN;
+  p->n_qtiles = (N + fa::BWD_DQ_BM - 1) / fa::BWD_DQ_BM;
+  p->n_ktiles = (N + fa::BWD_DKDV_BN - 1) / fa::BWD_DKDV_BN;
   p->xcd_grouped = plan->xcd_grouped;
   p->scale = scale;
   p->scale_log2 = scale * 1.4426950408889634f;
@@ -175,58 +176,63 @@ bool all_aligned(std::initializer_list<const void *> ptrs) {
 
 extern "C" {
 
-int fa_bwd_preprocess(const void *o, const void *dout, int B, int H, int N, int d, int dtype,
-                      void *workspace, size_t workspace_bytes, void *stream) {
-  if (!o || !dout || !workspace) return FA_ERR_NULL;
+int fa_bwd_preprocess(const void *o, const void *dout, const float *lse, int B, int H, int N,
+                      int d, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!o || !dout || !lse || !workspace) return FA_ERR_NULL;
   fa::BwdParams p;
   fa_plan_t plan;
   int rc = bwd_setup(B, H, N, d, 1.f, 0, dtype, workspace, workspace_bytes, &p, &plan);
   if (rc) return rc;
-  if (!all_aligned({o, dout})) return FA_ERR_ALIGN;
+  if (!all_aligned({o, dout, lse})) return FA_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
   p.o = o;
   p.dout = dout;
+  p.lse = lse;
   const hipError_t e = fa::launch_bwd_pre(p, dtype, d, (long)B * H * N,
                                           reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-int fa_bwd_main(const void *q, const void *k, const void *v, const void *dout, const float *lse,
-                void *dk, void *dv, int B, int H, int N, int d, float scale, int causal,
-                int dtype, void *workspace, size_t workspace_bytes, void *stream) {
-  if (!q || !k || !v || !dout || !lse || !dk || !dv || !workspace) return FA_ERR_NULL;
+int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, void *dk,
+                void *dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !dout || !dk || !dv || !workspace) return FA_ERR_NULL;
   fa::BwdParams p;
   fa_plan_t plan;
   int rc = bwd_setup(B, H, N, d, scale, causal, dtype, workspace, workspace_bytes, &p, &plan);
   if (rc) return rc;
-  if (!all_aligned({q, k, v, dout, lse, dk, dv})) return FA_ERR_ALIGN;
+  if (!all_aligned({q, k, v, dout, dk, dv})) return FA_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
   p.q = q;
   p.k = k;
   p.v = v;
   p.dout = dout;
-  p.lse = lse;
   p.dk = dk;
   p.dv = dv;
-  const hipError_t e = fa::launch_bwd_main(p, dtype, d, causal, plan.grid,
+  const hipError_t e = fa::launch_bwd_dkdv(p, dtype, d, causal, p.n_ktiles * B * H,
                                            reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-int fa_bwd_dq_convert(void *dq, int B, int H, int N, int d, float scale, int dtype,
-                      void *workspace, size_t workspace_bytes, void *stream) {
-  if (!dq || !workspace) return FA_ERR_NULL;
+int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, void *dq, int B,
+              int H, int N, int d, float scale, int causal, int dtype, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !dout || !dq || !workspace) return FA_ERR_NULL;
   fa::BwdParams p;
   fa_plan_t plan;
-  int rc = bwd_setup(B, H, N, d, scale, 0, dtype, workspace, workspace_bytes, &p, &plan);
+  int rc = bwd_setup(B, H, N, d, scale, causal, dtype, workspace, workspace_bytes, &p, &plan);
   if (rc) return rc;
-  if (!aligned16(dq)) return FA_ERR_ALIGN;
+  if (!all_aligned({q, k, v, dout, dq})) return FA_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dout = dout;
   p.dq = dq;
-  const hipError_t e = fa::launch_bwd_dq(p, dtype, (long)B * H * N * d,
+  const hipError_t e = fa::launch_bwd_dq(p, dtype, d, causal, p.n_qtiles * B * H,
                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -253,10 +259,9 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
   p.dk = dk;
   p.dv = dv;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const long rows = (long)B * H * N;
-  hipError_t e = fa::launch_bwd_pre(p, dtype, d, rows, st);
-  if (e == hipSuccess) e = fa::launch_bwd_main(p, dtype, d, causal, plan.grid, st);
-  if (e == hipSuccess) e = fa::launch_bwd_dq(p, dtype, rows * d, st);
+  hipError_t e = fa::launch_bwd_pre(p, dtype, d, (long)B * H * N, st);
+  if (e == hipSuccess) e = fa::launch_bwd_dkdv(p, dtype, d, causal, p.n_ktiles * B * H, st);
+  if (e == hipSuccess) e = fa::launch_bwd_dq(p, dtype, d, causal, p.n_qtiles * B * H, st);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -3,38 +3,62 @@
 // "Recomputation": P is not stored, it is rebuilt in the backward; its v2
 // section: the backward kernel's parallel schedule is what v2 reworked).
 //
-// Three kernels:
-//   bwd_pre_kernel   D_i = sum_c dO_ic O_ic (fp32) and a zeroed fp32 dQ accumulator
-//   bwd_kernel       one workgroup per (batch, head, 128-key tile); K_j and V_j stay
-//                    in registers, query tiles of 64 rows stream through LDS:
-//                      S = Q K_j^T, P = exp(scale S - LSE), dV_j += P^T dO,
-//                      dP = dO V_j^T, dS = P (dP - D), dK_j += dS^T Q,
-//                      dQ += dS K_j (fp32 atomics into the accumulator)
-//   bwd_dq_kernel    dQ = scale * accumulator, rounded to 16 bits
-// The gradient formulas are the calculus of O = softmax(scale Q K^T) V.
+// The gradients are the calculus of O = softmax(scale Q K^T) V:
+//   P = exp(scale S - LSE), dV = P^T dO, dP = dO V^T, D_i = rowsum(dO_i * O_i),
+//   dS = P (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
-// MFMA orientation: S and dP are computed as [query][key] tiles (A = Q or dO
-// fragments read from LDS, B = K^T or V^T fragments held in registers), so a
-// lane owns one key (l % 32) and 16 queries.  P and dS packed to 16 bits are
-// then directly the B operands of dV^T += dO^T P and dK^T += Q^T dS; the
-// dO^T / Q^T A operands come from LDS through ds_read_b64_tr_b16.  dS is also
-// written to LDS transposed ([key][query]) so that all four waves can form
-// dQ = dS K over the workgroup's 128 keys.
+// Three kernels, none with atomics (so every output is bitwise reproducible):
+//   bwd_pre_kernel   D = rowsum(dO * O) and LSE * log2(e), fp32 [B][H][N]
+//   bwd_dq_kernel    one workgroup per 128 query rows, K/V tiles streamed through
+//                    LDS (the forward's structure): S^T = K Q^T, dP^T = V dO^T,
+//                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T
+//   bwd_dkdv_kernel  one workgroup per 128 keys, Q/dO tiles streamed through LDS:
+//                    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS
+// P and dS are recomputed in both passes (two extra tile products compared with
+// a single pass that accumulates dQ with atomics), in exchange for no atomic
+// traffic, no fp32 dQ accumulator and deterministic results.
+//
+// MFMA orientation follows the forward: in the query-major pass a lane owns one
+// query and 16 keys of each 32x32 score block (the packed dS^T registers are
+// directly the B operand of dQ^T += K^T dS^T, whose A operand is read from LDS
+// with ds_read_b64_tr_b16); in the key-major pass a lane owns one key and 16
+// queries (packed P and dS are the B operands of dV^T += dO^T P and
+// dK^T += Q^T dS, with dO^T and Q^T read transposed from LDS).  Tiles reach LDS
+// by direct buffer->LDS loads one step ahead, with XOR-swizzled rows (see the
+// forward kernel).
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 
+namespace {
+
+// XOR swizzles of the 16-byte chunk index within a 256-byte (d = 128) or
+// 128-byte (d = 64) tile row.  FRAG: conflict-free for 16-byte fragment reads
+// of 32 consecutive rows; BOTH: also conflict-free for the transposing reads
+// of 4 consecutive rows.
+template <int D>
+__device__ __forceinline__ int swz_frag(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_both(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row & 3) << 1) ^ (row >> 2)) & 7);
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O) and zeroed dQ accumulator.  16 threads per row.
+// D = rowsum(dO * O) and LSE * log2(e).  16 threads per row.
 // ---------------------------------------------------------------------------
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict__ o,
                                                       const uint16_t *__restrict__ dout,
-                                                      float *__restrict__ Dws,
-                                                      float *__restrict__ dq_acc, long rows) {
-  constexpr int TPR = 16;            // threads per row
-  constexpr int EPT = D / TPR;       // elements per thread (8 or 4)
+                                                      const float *__restrict__ lse,
+                                                      float *__restrict__ dws,
+                                                      float *__restrict__ lse2, long rows) {
+  constexpr int TPR = 16;       // threads per row
+  constexpr int EPT = D / TPR;  // elements per thread (8 or 4)
   const long row = (long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int sub = threadIdx.x % TPR;
   float acc = 0.f;
@@ -50,56 +74,198 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc += T::lo(a[j]) * T::lo(b[j]) + T::hi(a[j]) * T::hi(b[j]);
     }
-    float *qa = dq_acc + row * D + sub * EPT;
-#pragma unroll
-    for (int j = 0; j < EPT; j += 4) *reinterpret_cast<f32x4 *>(qa + j) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && sub == 0) Dws[row] = acc;
-}
-
-// ---------------------------------------------------------------------------
-// dQ = scale * accumulator -> 16 bits.  4 elements per thread.
-// ---------------------------------------------------------------------------
-template <class T>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const float *__restrict__ dq_acc,
-                                                     uint16_t *__restrict__ dq, float scale,
-                                                     long n4) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i < n4) {
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(dq_acc + 4 * i);
-    u32x2 st;
-    st[0] = T::pack(a[0] * scale, a[1] * scale);
-    st[1] = T::pack(a[2] * scale, a[3] * scale);
-    *reinterpret_cast<u32x2 *>(dq + 4 * i) = st;
+  if (row < rows && sub == 0) {
+    dws[row] = acc;
+    lse2[row] = lse[row] * 1.4426950408889634f;
   }
 }
 
 // ---------------------------------------------------------------------------
-// main backward kernel
+// dQ: query-major pass
 // ---------------------------------------------------------------------------
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_kernel(BwdParams p) {
-  constexpr int BN = BWD_BN;          // keys per workgroup (32 per wave)
-  constexpr int BM = BWD_BM;          // query rows per inner step
-  constexpr int QS = D * 2 + 16;      // LDS row stride of Q / dO tiles (bytes)
-  constexpr int KS = D * 2 + 64;      // LDS row stride of the K tile
-  constexpr int SS = BM * 2 + 64;     // LDS row stride of the dS^T tile ([key][query])
-  constexpr int QT = BM * QS;         // bytes of one Q (or dO) tile
-  constexpr int STAGE = 2 * QT + 2 * BM * 4;  // Q, dO, LSE2, D
-  constexpr int OFF_K = 2 * STAGE;
-  constexpr int OFF_S = OFF_K + BN * KS;
-  constexpr int LDS_BYTES = OFF_S + BN * SS;
-  constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int CPT = BM * CPR / 256; // chunks per thread per Q (or dO) tile
-  constexpr int ND16 = D / 16, ND32 = D / 32, NQ32 = BM / 32, NQ16 = BM / 16;
-  static_assert(BM * CPR % 256 == 0, "tile must split evenly over 256 threads");
-  static_assert(BN == 128 && BM % 32 == 0, "tile shape");
-  static_assert((BM / 32) * (D / 32) % 4 == 0, "dQ blocks must split evenly over 4 waves");
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DQ_WAVES_PER_SIMD, BWD_DQ_WAVES_PER_SIMD)))
+void bwd_dq_kernel(BwdParams p) {
+  constexpr int BN = 32;                // keys per step
+  constexpr int BM = BWD_DQ_BM;         // query rows per workgroup (32 per wave)
+  constexpr int RB = D * 2;             // bytes per tile row
+  constexpr int TB = BN * RB;           // bytes per K (or V) tile
+  constexpr int OFF_V = 2 * TB;         // K ring (2 slots), then V ring (2 slots)
+  constexpr int CPR = RB / 16;
+  constexpr int ROWS_PER_BLOCK = 64 / CPR;
+  constexpr int BPW = TB / 1024 / 4;    // DMA blocks per wave per tile
+  constexpr int ND16 = D / 16, ND32 = D / 32;
+  static_assert(BPW >= 1 && BM == 128, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int g = lane >> 4, s16 = lane & 15;
+  const int N = p.N;
+
+  int bh, qt;
+  {
+    const int nq = p.n_qtiles;
+    const int bid = blockIdx.x;
+    int r;
+    if (p.xcd_grouped) {
+      const int x = bid & 7, kk = bid >> 3;
+      bh = x + 8 * (kk / nq);
+      r = kk % nq;
+    } else {
+      bh = bid / nq;
+      r = bid % nq;
+    }
+    qt = CAUSAL ? nq - 1 - r : r;  // causal: longest rows first
+  }
+  const int i0 = qt * BM;
+  const int wr0 = i0 + 32 * w;
+  const int qrow = wr0 + l32;  // this lane's query
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + hoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const uint16_t *>(p.dout) + hoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + hoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + hoff, head_bytes);
+
+  const int kend = CAUSAL ? min(N, i0 + BM) : N;
+  const int nt = (kend + BN - 1) / BN;
+  const float sl2 = p.scale_log2;
+
+  // per-lane row statistics; rows past N get lse2 = +inf so that P = 0
+  const float lse2 = qrow < N ? p.lse2[(size_t)bh * N + qrow] : __builtin_inff();
+  const float dsum = qrow < N ? p.dws[(size_t)bh * N + qrow] : 0.f;
+
+  // Q and dO fragments: B operands of S^T = K Q^T and dP^T = V dO^T
+  u32x4 qf[ND16], dof[ND16];
+#pragma unroll
+  for (int db = 0; db < ND16; ++db) {
+    const uint32_t off = (uint32_t)(qrow * D + db * 16 + hi * 8) * 2;  // rows past N read 0
+    qf[db] = bload16(rq, off);
+    dof[db] = bload16(rdo, off);
+  }
+
+  // K/V DMA into swizzled slots (K is read both ways, V only as fragments)
+  uint32_t dk_off[BPW], dv_off[BPW];
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int row = (w * BPW + j) * ROWS_PER_BLOCK + lane / CPR, pos = lane % CPR;
+    dk_off[j] = (uint32_t)(row * RB + ((pos ^ swz_both<D>(row)) << 4));
+    dv_off[j] = (uint32_t)(row * RB + ((pos ^ swz_frag<D>(row)) << 4));
+  }
+  auto issue_step = [&](int t) {  // tiles outside [0, nt) load as zeros
+    const bool ok = t >= 0 && t < nt;
+    const uint32_t base = ok ? (uint32_t)t * TB : 0x80000000u;
+    char *ks = smem + (t & 1) * TB;
+    char *vs = smem + OFF_V + (t & 1) * TB;
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      dma16(rk, ks + (w * BPW + j) * 1024, base + dk_off[j]);
+      dma16(rv, vs + (w * BPW + j) * 1024, base + dv_off[j]);
+    }
+  };
+
+  f32x16 dqacc[ND32];
+#pragma unroll
+  for (int c = 0; c < ND32; ++c) dqacc[c] = f32x16{};
+
+  const int f_sw = swz_frag<D>(l32), b_sw = swz_both<D>(l32);
+  const int t_row = 4 * (g >> 1) + (s16 >> 2);
+
+  issue_step(0);
+  wait_vmcnt<0>();
+  barrier_only();
+  for (int t = 0; t < nt; ++t) {
+    issue_step(t + 1);
+    const char *ks = smem + (t & 1) * TB;
+    const char *vs = smem + OFF_V + (t & 1) * TB;
+    // S^T = K Q^T and dP^T = V dO^T (keys x queries)
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int db = 0; db < ND16; ++db) {
+      const int ch = 2 * db + hi;
+      s = T::mma(lds_read16(ks + l32 * RB + ((ch ^ b_sw) << 4)), qf[db], s);
+      dp = T::mma(lds_read16(vs + l32 * RB + ((ch ^ f_sw) << 4)), dof[db], dp);
+    }
+    // P^T = exp2(scale log2e S - LSE log2e), masked; dS^T = P^T (dP^T - D)
+    const int j0 = t * BN;
+    const bool need_mask = (CAUSAL && j0 + BN - 1 > wr0) || (j0 + BN > N);
+    const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+    uint32_t dsk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * j + e;
+        float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lse2));
+        if (need_mask) {
+          const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          pr = key <= lim ? pr : 0.f;
+        }
+        v2[e] = pr * (dp[r] - dsum);
+      }
+      dsk[j] = T::pack(v2[0], v2[1]);
+    }
+    // dQ^T += K^T dS^T; K^T fragments by transposing reads of the K slot
+#pragma unroll
+    for (int c = 0; c < ND32; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int byte = c * 64 + 32 * (g & 1) + 8 * (s16 & 3);
+        const int r0 = kb * 16 + t_row;
+        const char *ap0 = ks + r0 * RB + (((byte >> 4) ^ swz_both<D>(r0)) << 4) + (byte & 15);
+        const char *ap1 = ks + (r0 + 8) * RB + (((byte >> 4) ^ swz_both<D>(r0 + 8)) << 4) + (byte & 15);
+        const u32x2 a0 = lds_read_tr4(ap0), a1 = lds_read_tr4(ap1);
+        const u32x4 b = {dsk[4 * kb], dsk[4 * kb + 1], dsk[4 * kb + 2], dsk[4 * kb + 3]};
+        dqacc[c] = T::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, b, dqacc[c]);
+      }
+    }
+    wait_vmcnt<0>();  // tiles for step t + 1 have landed
+    barrier_only();
+  }
+
+  // dQ = scale dQ^T^T, rounded to 16 bits
+  if (qrow < N) {
+    uint16_t *dQh = reinterpret_cast<uint16_t *>(p.dq) + hoff;
+    const float sc = p.scale;
+#pragma unroll
+    for (int c = 0; c < ND32; ++c)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int dcol = c * 32 + 8 * rg + 4 * hi;
+        u32x2 st;
+        st[0] = T::pack(dqacc[c][4 * rg] * sc, dqacc[c][4 * rg + 1] * sc);
+        st[1] = T::pack(dqacc[c][4 * rg + 2] * sc, dqacc[c][4 * rg + 3] * sc);
+        *reinterpret_cast<u32x2 *>(dQh + (size_t)qrow * D + dcol) = st;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: key-major pass
+// ---------------------------------------------------------------------------
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DKDV_WAVES_PER_SIMD, BWD_DKDV_WAVES_PER_SIMD)))
+void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BM = BWD_DKDV_BM;       // query rows per step
+  constexpr int BN = BWD_DKDV_BN;       // keys per workgroup (32 per wave)
+  constexpr int RB = D * 2;
+  constexpr int TB = BM * RB;           // bytes per Q (or dO) tile
+  constexpr int STAT = 512;             // LSE2 (64 floats read, 32 used), then D
+  constexpr int SLOT = 2 * TB + STAT;   // Q, dO, stats
+  constexpr int CPR = RB / 16;
+  constexpr int ROWS_PER_BLOCK = 64 / CPR;
+  constexpr int BPW = TB / 1024 / 4;
+  constexpr int ND16 = D / 16, ND32 = D / 32;
+  static_assert(BPW >= 1 && BM == 32 && BN == 128, "tile shape");
+
+  __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -122,225 +288,130 @@ void bwd_kernel(BwdParams p) {
     // causal: key tile 0 sees every query tile, so ascending order is heavy-first
   }
   const int j0 = kt * BN;
-  const int kw0 = j0 + 32 * w;  // first key of this wave
+  const int kw0 = j0 + 32 * w;
+  const int key = kw0 + l32;  // this lane's key
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + hoff;
-  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + hoff;
-  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + hoff;
-  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + hoff;
-  const float *Lh = p.lse + (size_t)bh * N;
-  const float *Dh = p.dws + (size_t)bh * N;
-  float *dQa = p.dq_acc + hoff;
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const uint32_t stat_bytes = (uint32_t)N * 4;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + hoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const uint16_t *>(p.dout) + hoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + hoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + hoff, head_bytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse2 + (size_t)bh * N, stat_bytes);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dws + (size_t)bh * N, stat_bytes);
 
-  // ---- K, V fragments of this wave's 32 keys (B operands of Q K^T and dO V^T)
+  // K and V fragments of this wave's keys: B operands of S = Q K^T, dP = dO V^T
   u32x4 kf[ND16], vf[ND16];
-  {
-    const int key = kw0 + l32;
 #pragma unroll
-    for (int db = 0; db < ND16; ++db) {
-      const size_t off = (size_t)key * D + db * 16 + hi * 8;
-      kf[db] = key < N ? gload16(Kh + off) : u32x4{0, 0, 0, 0};
-      vf[db] = key < N ? gload16(Vh + off) : u32x4{0, 0, 0, 0};
-    }
-  }
-  // ---- the workgroup's K tile in LDS (B operand of dQ = dS K, transposing reads)
-  {
-    constexpr int KCPT = BN * CPR / 256;
-#pragma unroll
-    for (int c = 0; c < KCPT; ++c) {
-      const int ch = tid + 256 * c;
-      const int row = ch / CPR, col = ch % CPR;
-      const u32x4 val = j0 + row < N ? gload16(Kh + (size_t)(j0 + row) * D + col * 8) : u32x4{0, 0, 0, 0};
-      lds_write16(smem + OFF_K + row * KS + col * 16, val);
-    }
-  }
-
-  f32x16 dvacc[ND32], dkacc[ND32];
-#pragma unroll
-  for (int c = 0; c < ND32; ++c) {
-    dvacc[c] = f32x16{};
-    dkacc[c] = f32x16{};
+  for (int db = 0; db < ND16; ++db) {
+    const uint32_t off = (uint32_t)(key * D + db * 16 + hi * 8) * 2;  // keys past N read 0
+    kf[db] = bload16(rk, off);
+    vf[db] = bload16(rv, off);
   }
 
   const int nqt = (N + BM - 1) / BM;
   const int qt0 = CAUSAL ? j0 / BM : 0;
   const float sl2 = p.scale_log2;
 
-  // ---- Q / dO tile staging: global -> registers -> LDS
-  u32x4 pre[2 * CPT];
-  float pre_l = 0.f, pre_d = 0.f;
-  auto gfetch = [&](int qt) {
-    const int q0 = qt * BM;
+  uint32_t dq_off[BPW];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + 256 * c;
-      const int row = ch / CPR, col = ch % CPR;
-      const bool ok = q0 + row < N;
-      const size_t off = (size_t)(q0 + row) * D + col * 8;
-      pre[c] = ok ? gload16(Qh + off) : u32x4{0, 0, 0, 0};
-      pre[CPT + c] = ok ? gload16(dOh + off) : u32x4{0, 0, 0, 0};
-    }
-    if (tid < BM) {
-      const bool ok = q0 + tid < N;
-      // rows past the end get LSE = +inf so that their P is exactly 0
-      pre_l = ok ? Lh[q0 + tid] * 1.4426950408889634f : __builtin_inff();
-      pre_d = ok ? Dh[q0 + tid] : 0.f;
-    }
-  };
-  auto lstore = [&](int stage) {
-    char *qs = smem + stage * STAGE;
-    char *ds = qs + QT;
-    float *ls = reinterpret_cast<float *>(qs + 2 * QT);
+  for (int j = 0; j < BPW; ++j) {
+    const int row = (w * BPW + j) * ROWS_PER_BLOCK + lane / CPR, pos = lane % CPR;
+    dq_off[j] = (uint32_t)(row * RB + ((pos ^ swz_both<D>(row)) << 4));
+  }
+  // step i loads query tile qt0 + i into slot i & 1: Q, dO (swizzled), LSE2, D
+  auto issue_step = [&](int i) {
+    const int qtile = qt0 + i;
+    const bool ok = qtile < nqt;
+    const uint32_t base = ok ? (uint32_t)qtile * TB : 0x80000000u;
+    char *slot = smem + (i & 1) * SLOT;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + 256 * c;
-      const int row = ch / CPR, col = ch % CPR;
-      lds_write16(qs + row * QS + col * 16, pre[c]);
-      lds_write16(ds + row * QS + col * 16, pre[CPT + c]);
+    for (int j = 0; j < BPW; ++j) {
+      dma16(rq, slot + (w * BPW + j) * 1024, base + dq_off[j]);
+      dma16(rdo, slot + TB + (w * BPW + j) * 1024, base + dq_off[j]);
     }
-    if (tid < BM) {
-      ls[tid] = pre_l;
-      ls[BM + tid] = pre_d;
+    if (w == 0) {  // 64 lanes x 4 bytes each: rows qtile*BM + lane (the first 32 are used)
+      const uint32_t so = ok ? (uint32_t)(qtile * BM + lane) * 4 : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void *)(slot + 2 * TB), 4, so, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void *)(slot + 2 * TB + 256), 4, so, 0, 0, 0);
     }
   };
 
-  gfetch(qt0);
-  lstore(0);
-  __syncthreads();
-
-  char *sT = smem + OFF_S;  // dS^T tile, [key][query] 16-bit
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int it = qt - qt0;
-    if (qt + 1 < nqt) gfetch(qt + 1);
-    const char *qs = smem + (it & 1) * STAGE;
-    const char *ds = qs + QT;
-    const float *ls = reinterpret_cast<const float *>(qs + 2 * QT);
-    const float *dsum = ls + BM;
-    const int q0 = qt * BM;
-    const bool active = !CAUSAL || q0 + BM - 1 >= kw0;
-    if (active) {
-      // -- S = Q K^T and dP = dO V^T, [query][key], NQ32 blocks of 32 queries
-      f32x16 s[NQ32], dp[NQ32];
+  f32x16 dkacc[ND32], dvacc[ND32];
 #pragma unroll
-      for (int qb = 0; qb < NQ32; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
-      }
-#pragma unroll
-      for (int db = 0; db < ND16; ++db)
-#pragma unroll
-        for (int qb = 0; qb < NQ32; ++qb) {
-          const int off = (qb * 32 + l32) * QS + db * 32 + hi * 16;
-          s[qb] = T::mma(lds_read16(qs + off), kf[db], s[qb]);
-          dp[qb] = T::mma(lds_read16(ds + off), vf[db], dp[qb]);
-        }
-      // -- P = exp2(S scale log2e - LSE log2e), dS = P (dP - D); masked entries 0
-      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N);
-      const int key = kw0 + l32;
-      uint32_t pk[NQ16][4], sk[NQ16][4];
-#pragma unroll
-      for (int qb = 0; qb < NQ32; ++qb) {
-        float pv[16], dsv[16];
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int qr = qb * 32 + 8 * rg + 4 * hi;  // 4 consecutive query rows
-          const f32x4 lq = *reinterpret_cast<const f32x4 *>(ls + qr);
-          const f32x4 dq = *reinterpret_cast<const f32x4 *>(dsum + qr);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e;
-            float pr = fast_exp2(__builtin_fmaf(s[qb][r], sl2, -lq[e]));
-            if (need_mask) {
-              const int qrow = q0 + qr + e;
-              if ((CAUSAL && key > qrow) || key >= N) pr = 0.f;
-            }
-            pv[r] = pr;
-            dsv[r] = pr * (dp[qb][r] - dq[e]);
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pk[qb * 2 + h][j] = T::pack(pv[8 * h + 2 * j], pv[8 * h + 2 * j + 1]);
-            sk[qb * 2 + h][j] = T::pack(dsv[8 * h + 2 * j], dsv[8 * h + 2 * j + 1]);
-          }
-      }
-      // -- dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing LDS reads)
-#pragma unroll
-      for (int c = 0; c < ND32; ++c)
-#pragma unroll
-        for (int kb = 0; kb < NQ16; ++kb) {
-          const int qrow = kb * 16 + 4 * (g >> 1) + (s16 >> 2);
-          const int col = c * 32 + 16 * (g & 1) + 4 * (s16 & 3);
-          const int off = qrow * QS + col * 2;
-          const u32x2 d0 = lds_read_tr4(ds + off), d1 = lds_read_tr4(ds + off + 8 * QS);
-          const u32x2 q0v = lds_read_tr4(qs + off), q1v = lds_read_tr4(qs + off + 8 * QS);
-          const u32x4 ad = {d0[0], d0[1], d1[0], d1[1]};
-          const u32x4 aq = {q0v[0], q0v[1], q1v[0], q1v[1]};
-          const u32x4 bp = {pk[kb][0], pk[kb][1], pk[kb][2], pk[kb][3]};
-          const u32x4 bs = {sk[kb][0], sk[kb][1], sk[kb][2], sk[kb][3]};
-          dvacc[c] = T::mma(ad, bp, dvacc[c]);
-          dkacc[c] = T::mma(aq, bs, dkacc[c]);
-        }
-      // -- dS^T to LDS: row = key (32 w + l32), 4 consecutive queries per write
-#pragma unroll
-      for (int kb = 0; kb < NQ16; ++kb)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          // registers 8h..8h+7 of block qb hold queries qb*32 + 16h + 8*(j/4) + 4*hi + j%4
-          const int qcol = kb * 16 + 8 * h2 + 4 * hi;
-          u32x2 v2 = {sk[kb][2 * h2], sk[kb][2 * h2 + 1]};
-          *reinterpret_cast<u32x2 *>(sT + (32 * w + l32) * SS + qcol * 2) = v2;
-        }
-    } else {
-      // every query of this tile precedes every key of this wave: dS = 0
-#pragma unroll
-      for (int kb = 0; kb < NQ16; ++kb)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int qcol = kb * 16 + 8 * h2 + 4 * hi;
-          *reinterpret_cast<u32x2 *>(sT + (32 * w + l32) * SS + qcol * 2) = u32x2{0u, 0u};
-        }
-    }
-    __syncthreads();
-    // -- dQ[q][d] += sum_key dS[q][key] K[key][d] over the workgroup's keys; the
-    //    (32-query, 32-column) blocks of the dQ tile are dealt round-robin to the waves
-    if (!CAUSAL || q0 + BM - 1 >= j0) {
-#pragma unroll
-      for (int u = w; u < NQ32 * ND32; u += 4) {
-        const int qb = u / ND32, c = u % ND32;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int kb = 0; kb < BN / 16; ++kb) {
-          // A = dS (query x key): rows of dS^T are keys -> transposing read
-          const int krow = kb * 16 + 4 * (g >> 1) + (s16 >> 2);
-          const int qcol = qb * 32 + 16 * (g & 1) + 4 * (s16 & 3);
-          const char *ap = sT + krow * SS + qcol * 2;
-          const u32x2 a0 = lds_read_tr4(ap), a1 = lds_read_tr4(ap + 8 * SS);
-          // B = K (key x d): transposing read of the K tile
-          const int dcol = 32 * c + 16 * (g & 1) + 4 * (s16 & 3);
-          const char *bp = smem + OFF_K + krow * KS + dcol * 2;
-          const u32x2 b0 = lds_read_tr4(bp), b1 = lds_read_tr4(bp + 8 * KS);
-          acc = T::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, u32x4{b0[0], b0[1], b1[0], b1[1]}, acc);
-        }
-        // acc[r]: query qb*32 + 8*(r/4) + 4*hi + r%4, d column 32c + l32
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow = q0 + qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (qrow < N) atomicAdd(dQa + (size_t)qrow * D + 32 * c + l32, acc[r]);
-        }
-      }
-    }
-    if (qt + 1 < nqt) lstore((it + 1) & 1);
-    __syncthreads();
+  for (int c = 0; c < ND32; ++c) {
+    dkacc[c] = f32x16{};
+    dvacc[c] = f32x16{};
   }
 
-  // ---- epilogue: dK = scale dK^T^T, dV = dV^T^T, rounded to 16 bits
-  uint16_t *dKh = reinterpret_cast<uint16_t *>(p.dk) + hoff;
-  uint16_t *dVh = reinterpret_cast<uint16_t *>(p.dv) + hoff;
-  const int key = kw0 + l32;
+  const int f_sw = swz_both<D>(l32);
+  const int t_row = 4 * (g >> 1) + (s16 >> 2);
+
+  const int nsteps = nqt - qt0;
+  issue_step(0);
+  wait_vmcnt<0>();
+  barrier_only();
+  for (int i = 0; i < nsteps; ++i) {
+    issue_step(i + 1);
+    const char *qs = smem + (i & 1) * SLOT;
+    const char *ds = qs + TB;
+    const float *ls = reinterpret_cast<const float *>(qs + 2 * TB);  // LSE2 at [0, 32), D at [64, 96)
+    const int q0 = (qt0 + i) * BM;
+    // S = Q K^T and dP = dO V^T (queries x keys): lane = key, registers = queries
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int db = 0; db < ND16; ++db) {
+      const int off = l32 * RB + (((2 * db + hi) ^ f_sw) << 4);
+      s = T::mma(lds_read16(qs + off), kf[db], s);
+      dp = T::mma(lds_read16(ds + off), vf[db], dp);
+    }
+    const bool need_mask = CAUSAL && q0 < kw0 + 31;
+    uint32_t pk[8], sk[8];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int qr = 8 * rg + 4 * hi;  // 4 consecutive query rows of this register group
+      const f32x4 lq = *reinterpret_cast<const f32x4 *>(ls + qr);
+      const f32x4 dq = *reinterpret_cast<const f32x4 *>(ls + 64 + qr);
+      float pv[4], sv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        // rows past N load LSE2 = D = 0 and Q = dO = 0, so they contribute nothing
+        float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lq[e]));
+        if (need_mask) pr = key <= q0 + qr + e ? pr : 0.f;
+        pv[e] = pr;
+        sv[e] = pr * (dp[r] - dq[e]);
+      }
+      pk[2 * rg] = T::pack(pv[0], pv[1]);
+      pk[2 * rg + 1] = T::pack(pv[2], pv[3]);
+      sk[2 * rg] = T::pack(sv[0], sv[1]);
+      sk[2 * rg + 1] = T::pack(sv[2], sv[3]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing reads)
+#pragma unroll
+    for (int c = 0; c < ND32; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int byte = c * 64 + 32 * (g & 1) + 8 * (s16 & 3);
+        const int r0 = kb * 16 + t_row;
+        const int o0 = r0 * RB + (((byte >> 4) ^ swz_both<D>(r0)) << 4) + (byte & 15);
+        const int o1 = (r0 + 8) * RB + (((byte >> 4) ^ swz_both<D>(r0 + 8)) << 4) + (byte & 15);
+        const u32x2 d0 = lds_read_tr4(ds + o0), d1 = lds_read_tr4(ds + o1);
+        const u32x2 q0v = lds_read_tr4(qs + o0), q1v = lds_read_tr4(qs + o1);
+        const u32x4 bp = {pk[4 * kb], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
+        const u32x4 bs = {sk[4 * kb], sk[4 * kb + 1], sk[4 * kb + 2], sk[4 * kb + 3]};
+        dvacc[c] = T::mma(u32x4{d0[0], d0[1], d1[0], d1[1]}, bp, dvacc[c]);
+        dkacc[c] = T::mma(u32x4{q0v[0], q0v[1], q1v[0], q1v[1]}, bs, dkacc[c]);
+      }
+    }
+    wait_vmcnt<0>();  // tiles for step i + 1 have landed
+    barrier_only();
+  }
+
+  // dK = scale dK^T^T, dV = dV^T^T, rounded to 16 bits
   if (key < N) {
+    uint16_t *dKh = reinterpret_cast<uint16_t *>(p.dk) + hoff;
+    uint16_t *dVh = reinterpret_cast<uint16_t *>(p.dv) + hoff;
     const float sc = p.scale;
 #pragma unroll
     for (int c = 0; c < ND32; ++c)
@@ -367,24 +438,25 @@ static hipError_t launch_pre_t(const BwdParams &p, long rows, hipStream_t st) {
   const int grid = (int)((rows + 15) / 16);
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(grid), dim3(256), 0, st,
                      reinterpret_cast<const uint16_t *>(p.o),
-                     reinterpret_cast<const uint16_t *>(p.dout), p.dws, p.dq_acc, rows);
+                     reinterpret_cast<const uint16_t *>(p.dout), p.lse, p.dws, p.lse2, rows);
   return hipGetLastError();
 }
 
 template <class T, int D>
-static hipError_t launch_main_t(const BwdParams &p, int causal, int grid, hipStream_t st) {
+static hipError_t launch_dq_t(const BwdParams &p, int causal, int grid, hipStream_t st) {
   if (causal)
-    hipLaunchKernelGGL((bwd_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((bwd_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-template <class T>
-static hipError_t launch_dq_t(const BwdParams &p, long elems, hipStream_t st) {
-  const long n4 = elems / 4;
-  hipLaunchKernelGGL((bwd_dq_kernel<T>), dim3((int)((n4 + 255) / 256)), dim3(256), 0, st,
-                     p.dq_acc, reinterpret_cast<uint16_t *>(p.dq), p.scale, n4);
+template <class T, int D>
+static hipError_t launch_dkdv_t(const BwdParams &p, int causal, int grid, hipStream_t st) {
+  if (causal)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -393,15 +465,18 @@ hipError_t launch_bwd_pre(const BwdParams &p, int dtype, int d, long rows, hipSt
   return d == 128 ? launch_pre_t<F16, 128>(p, rows, st) : launch_pre_t<F16, 64>(p, rows, st);
 }
 
-hipError_t launch_bwd_main(const BwdParams &p, int dtype, int d, int causal, int grid,
-                           hipStream_t st) {
+hipError_t launch_bwd_dq(const BwdParams &p, int dtype, int d, int causal, int grid,
+                         hipStream_t st) {
   if (dtype == 1)
-    return d == 128 ? launch_main_t<BF16, 128>(p, causal, grid, st) : launch_main_t<BF16, 64>(p, causal, grid, st);
-  return d == 128 ? launch_main_t<F16, 128>(p, causal, grid, st) : launch_main_t<F16, 64>(p, causal, grid, st);
+    return d == 128 ? launch_dq_t<BF16, 128>(p, causal, grid, st) : launch_dq_t<BF16, 64>(p, causal, grid, st);
+  return d == 128 ? launch_dq_t<F16, 128>(p, causal, grid, st) : launch_dq_t<F16, 64>(p, causal, grid, st);
 }
 
-hipError_t launch_bwd_dq(const BwdParams &p, int dtype, long elems, hipStream_t st) {
-  return dtype == 1 ? launch_dq_t<BF16>(p, elems, st) : launch_dq_t<F16>(p, elems, st);
+hipError_t launch_bwd_dkdv(const BwdParams &p, int dtype, int d, int causal, int grid,
+                           hipStream_t st) {
+  if (dtype == 1)
+    return d == 128 ? launch_dkdv_t<BF16, 128>(p, causal, grid, st) : launch_dkdv_t<BF16, 64>(p, causal, grid, st);
+  return d == 128 ? launch_dkdv_t<F16, 128>(p, causal, grid, st) : launch_dkdv_t<F16, 64>(p, causal, grid, st);
 }
 
 }  // namespace fa

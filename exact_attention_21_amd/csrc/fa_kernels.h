@@ -33,30 +33,40 @@ struct FwdParams {
   float scale_log2; // scale * log2(e)
 };
 
-// Backward tiling: keys per workgroup and query rows per inner step.
-constexpr int BWD_BN = 128;
-constexpr int BWD_BM = 64;
+// Backward tiling.  dQ pass: 128 query rows per workgroup, 32 keys per step.
+// dK/dV pass: 128 keys per workgroup, 32 query rows per step.
+constexpr int BWD_DQ_BM = 128;
+constexpr int BWD_DKDV_BN = 128;
+constexpr int BWD_DKDV_BM = 32;
+#ifndef BWD_DQ_WAVES_PER_SIMD
+#define BWD_DQ_WAVES_PER_SIMD 2
+#endif
+#ifndef BWD_DKDV_WAVES_PER_SIMD
+#define BWD_DKDV_WAVES_PER_SIMD 1
+#endif
 
 struct BwdParams {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
-  float *dq_acc;    // fp32 [B][H][N][d] workspace
   float *dws;       // fp32 [B][H][N] workspace: D = rowsum(dO * O)
+  float *lse2;      // fp32 [B][H][N] workspace: LSE * log2(e)
   int N;
-  int n_ktiles;     // ceil(N / BWD_BN)
+  int n_qtiles;     // ceil(N / BWD_DQ_BM)
+  int n_ktiles;     // ceil(N / BWD_DKDV_BN)
   int xcd_grouped;
   float scale;
   float scale_log2;
 };
 
-// D = rowsum(dO * O) and zeroed dQ accumulator (reads p.o, p.dout; writes p.dws, p.dq_acc)
+// D = rowsum(dO * O) and LSE * log2(e) (reads p.o, p.dout, p.lse; writes p.dws, p.lse2)
 hipError_t launch_bwd_pre(const BwdParams &p, int dtype, int d, long rows, hipStream_t st);
-// main backward kernel (writes p.dk, p.dv, accumulates p.dq_acc)
-hipError_t launch_bwd_main(const BwdParams &p, int dtype, int d, int causal, int grid,
+// dQ pass (reads q, k, v, dout, dws, lse2; writes dq); grid = n_qtiles * B * H
+hipError_t launch_bwd_dq(const BwdParams &p, int dtype, int d, int causal, int grid,
+                         hipStream_t st);
+// dK/dV pass (reads q, k, v, dout, dws, lse2; writes dk, dv); grid = n_ktiles * B * H
+hipError_t launch_bwd_dkdv(const BwdParams &p, int dtype, int d, int causal, int grid,
                            hipStream_t st);
-// dQ = scale * accumulator -> 16 bits (reads p.dq_acc, writes p.dq)
-hipError_t launch_bwd_dq(const BwdParams &p, int dtype, long elems, hipStream_t st);
 
 hipError_t launch_fwd(const FwdParams &p, int dtype, int d, int causal, int qb, int grid,
                       hipStream_t st);

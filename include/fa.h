@@ -72,9 +72,8 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            void *stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: an fp32 dQ accumulator [B][H][N][d]
- * and D = rowsum(dO * O) fp32 [B][H][N], each 256-byte aligned.  Returns 0 for
- * invalid shapes.
+ * Bytes of device workspace fa_bwd needs: D = rowsum(dO * O) and LSE * log2(e),
+ * each fp32 [B][H][N] and 256-byte aligned.  Returns 0 for invalid shapes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -87,8 +86,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * definition above:
  *   P = softmax(scale Q K^T [mask]), dV = P^T dO, dP = dO V^T,
  *   D_i = rowsum(dO_i * O_i), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
- * dK and dV are bitwise reproducible; dQ is accumulated with fp32 atomics and
- * may differ run to run in the last bits.
+ * No atomics are used: dq, dk and dv are bitwise reproducible run to run.
  * `workspace` must hold fa_bwd_workspace_size(B,H,N,d) bytes (16-byte aligned);
  * its contents on entry do not matter and are clobbered.
  */
@@ -98,26 +96,26 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * The three stages fa_bwd runs, in order, on one stream; exposed so that a
- * caller can schedule or time them separately.  They share fa_bwd's argument
- * rules and workspace layout; fa_bwd(...) is exactly
- *   fa_bwd_preprocess -> fa_bwd_main -> fa_bwd_dq_convert.
+ * The three stages fa_bwd runs on one stream, exposed so that a caller can
+ * schedule or time them separately.  They share fa_bwd's argument rules and
+ * workspace layout; fa_bwd(...) is exactly
+ *   fa_bwd_preprocess -> fa_bwd_dkdv -> fa_bwd_dq
+ * (the last two only read the workspace and may run in either order).
  *
- * fa_bwd_preprocess: reads o and dout; writes D_i = sum_c dO_ic O_ic (fp32) into
- *   the workspace and zeroes its fp32 dQ accumulator.
- * fa_bwd_main: recomputes P from q, k and lse (scale and causal as in the
- *   forward), writes dk and dv, and adds dS K into the workspace's dQ
- *   accumulator with fp32 atomics.  Needs fa_bwd_preprocess's workspace.
- * fa_bwd_dq_convert: writes dq = scale * accumulator, rounded to `dtype`.
+ * fa_bwd_preprocess: reads o, dout and lse; writes D_i = sum_c dO_ic O_ic and
+ *   lse * log2(e) (fp32) into the workspace.
+ * fa_bwd_dkdv: recomputes P and dS key-block by key-block; writes dk and dv.
+ * fa_bwd_dq: recomputes P and dS query-block by query-block; writes dq.
  */
-int fa_bwd_preprocess(const void *o, const void *dout, int B, int H, int N, int d,
-                      int dtype, void *workspace, size_t workspace_bytes, void *stream);
-int fa_bwd_main(const void *q, const void *k, const void *v, const void *dout,
-                const float *lse, void *dk, void *dv, int B, int H, int N, int d,
-                float scale, int causal, int dtype, void *workspace,
-                size_t workspace_bytes, void *stream);
-int fa_bwd_dq_convert(void *dq, int B, int H, int N, int d, float scale, int dtype,
-                      void *workspace, size_t workspace_bytes, void *stream);
+int fa_bwd_preprocess(const void *o, const void *dout, const float *lse, int B, int H,
+                      int N, int d, int dtype, void *workspace, size_t workspace_bytes,
+                      void *stream);
+int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, void *dk,
+                void *dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, void *dq,
+              int B, int H, int N, int d, float scale, int causal, int dtype,
+              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Launch plan of a forward call (host-only, no GPU needed). */
 typedef struct {
@@ -134,8 +132,8 @@ typedef struct {
 int fa_fwd_plan(int B, int H, int N, int d, int causal, int dtype,
                 fa_plan_t *plan);
 
-/* Fills *plan for the main backward kernel (block_m = query rows per inner
- * step, block_n = keys per workgroup). */
+/* Fills *plan for the dK/dV pass of the backward (block_m = query rows per
+ * inner step, block_n = keys per workgroup). */
 int fa_bwd_plan(int B, int H, int N, int d, int causal, int dtype,
                 fa_plan_t *plan);
 
