@@ -36,6 +36,35 @@ WORKLOAD = dict(name="c3_fwd_bwd_causal_n8192_d128_bf16", B=4, H=32, N=8192, d=1
                 causal=True)
 
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
+# workload (FETCH_SIZE scaled x2.0, WRITE_SIZE x1.0 by a plain 1 GiB copy; see
+# profiles/fwd_bwd_causal_n8192_d128_bf16_hbm_traffic.md).  Valid only for the
+# kernel sources they were taken on: the hash of those sources must match.
+MEASURED_TRAFFIC = {
+    "source_sha256_16": "bf0f2b12c9b16085",
+    "bytes": {"fwd_kernel": 1.4086e9, "bwd_pre_kernel": 0.5537e9,
+              "bwd_dkdv_kernel": 2.0702e9, "bwd_dq_kernel": 1.5260e9},
+}
+KERNEL_SOURCES = ["exact_attention_21_amd/csrc/fa_bwd.hip", "exact_attention_21_amd/csrc/fa_fwd.hip",
+                  "exact_attention_21_amd/csrc/fa_device.h", "exact_attention_21_amd/csrc/fa_kernels.h",
+                  "exact_attention_21_amd/build.py"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    if kernel_source_hash() != MEASURED_TRAFFIC["source_sha256_16"]:
+        return None  # kernels changed since the counters were taken
+    return MEASURED_TRAFFIC["bytes"].get(kernel)
+
+
 def nominal_flop(B, H, N, d, causal):
     f = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
     return f, 2.5 * f
@@ -190,7 +219,7 @@ def main():
     dom_ms, dom_flop = kern[dom]
     dom_tf = dom_flop / (dom_ms * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": dom_tf, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": dom_tf / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": dom_tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
                 "avg_launch_ms": dom_ms, "algorithmic_flop_per_launch": dom_flop}
     kernels = {n: {"avg_ms": ms, "tflops": (fl / (ms * 1e-3) / 1e12) if fl else None,
                    "frac_of_peak": (fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if fl else None}

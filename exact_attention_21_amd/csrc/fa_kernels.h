@@ -42,7 +42,7 @@ constexpr int BWD_DKDV_BM = 32;
 #define BWD_DQ_WAVES_PER_SIMD 2
 #endif
 #ifndef BWD_DKDV_WAVES_PER_SIMD
-#define BWD_DKDV_WAVES_PER_SIMD 1
+#define BWD_DKDV_WAVES_PER_SIMD 2
 #endif
 
 struct BwdParams {
