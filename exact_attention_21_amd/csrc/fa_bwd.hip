@@ -103,7 +103,8 @@ void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, keep in an SGPR
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = lane >> 4, s16 = lane & 15;
   const int N = p.N;
@@ -268,7 +269,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, keep in an SGPR
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = lane >> 4, s16 = lane & 15;
   const int N = p.N;

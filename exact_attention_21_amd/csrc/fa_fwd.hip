@@ -37,6 +37,8 @@
 // exponentials are taken against a stale max, so p <= 2^8; the final
 // normalisation uses the same stale max in numerator and denominator, so the
 // result is unchanged.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -45,8 +47,7 @@ namespace fa {
 namespace {
 
 constexpr float LAZY_TAU = 8.0f;  // log2 growth of a row max that forces a rescale
-constexpr int PREFETCH = 1;       // steps between issuing a tile's load and its use
-constexpr int NSLOT = PREFETCH + 1;
+constexpr int NSLOT = 2;          // ring slots per K and V (tiles are loaded one step ahead)
 
 // o *= a for an accumulator that lives in AGPRs (rare path): read, scale and
 // write back each register without moving the accumulator out of AGPRs.
@@ -66,10 +67,19 @@ template <int D>
 __device__ __forceinline__ int swz_k(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
+// The V swizzle depends on row bits 0..3 only: the fragment reads add 16 rows
+// to a precomputed address for the second 16-key half of a tile.
 template <int D>
-__device__ __forceinline__ int swz_v(int row) {
-  return ((row & 3) << 1) & (D / 8 - 1);
+__host__ __device__ constexpr int swz_v(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row & 3) << 1) ^ ((row >> 2) & 3)) & 7);
 }
+template <int D>
+constexpr bool swz_v_period16() {
+  for (int r = 0; r < 16; ++r)
+    if (swz_v<D>(r + 16) != swz_v<D>(r)) return false;
+  return true;
+}
+static_assert(swz_v_period16<64>() && swz_v_period16<128>(), "V swizzle must repeat every 16 rows");
 
 }  // namespace
 
@@ -93,7 +103,8 @@ void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, keep in an SGPR
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = lane >> 4, s16 = lane & 15;
   const int N = p.N;
@@ -170,20 +181,34 @@ void fwd_kernel(FwdParams p) {
   f32x16 sacc[QB];
   uint32_t pk[QB][8];
 
-  // fragment-read addresses inside a slot
-  const int k_rd = l32 * RB;
-  const int k_sw = swz_k<D>(l32);
-  const int v_row = 4 * (g >> 1) + (s16 >> 2);  // + 16 kb (+ 8 for the second read)
-  const int v_sw = swz_v<D>(v_row);             // row & 3 is unchanged by +16 kb and +8
+  // fragment-read byte offsets inside a slot, computed once (the slot base is a
+  // compile-time constant in the two-way unrolled loop below)
+  uint32_t k_addr[ND16];
+#pragma unroll
+  for (int db = 0; db < ND16; ++db)
+    k_addr[db] = (uint32_t)(l32 * RB + (((2 * db + hi) ^ swz_k<D>(l32)) << 4));
+  uint32_t v_addr[ND32][2];  // [32-column block][first / second 4-row read]
+  {
+    const int v_row = 4 * (g >> 1) + (s16 >> 2);  // + 16 kb for the second 16-key half
+#pragma unroll
+    for (int c = 0; c < ND32; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = v_row + 8 * h;  // swz_v(row + 16) == swz_v(row)
+        const int byte = c * 64 + 32 * (g & 1) + 8 * (s16 & 3);
+        v_addr[c][h] = (uint32_t)(row * RB + (((byte >> 4) ^ swz_v<D>(row)) << 4) + (byte & 15));
+      }
+  }
 
-  // S(t) = K(t) Q^T
-  auto stage_s = [&](int t, f32x16 (&s)[QB]) {
-    const char *ks = smem + (t % NSLOT) * TB;
+  // S(t) = K(t) Q^T, K(t) in ring slot SL
+  auto stage_s = [&](auto slot, f32x16 (&s)[QB]) {
+    constexpr int SL = decltype(slot)::value;
+    const char *ks = smem + SL * TB;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
     for (int db = 0; db < ND16; ++db) {
-      const u32x4 a = lds_read16(ks + k_rd + (((2 * db + hi) ^ k_sw) << 4));
+      const u32x4 a = lds_read16(ks + k_addr[db]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb] = T::mma(a, qf[qb][db], s[qb]);
     }
@@ -235,17 +260,16 @@ void fwd_kernel(FwdParams p) {
     }
     return grow_any;
   };
-  // O^T += V(t)^T P(t)^T
-  auto stage_pv = [&](int t, const uint32_t (&pk)[QB][8]) {
-    const char *vs = smem + OFF_V + (t % NSLOT) * TB;
+  // O^T += V(t)^T P(t)^T, V(t) in ring slot SL
+  auto stage_pv = [&](auto slot, const uint32_t (&pk)[QB][8]) {
+    constexpr int SL = decltype(slot)::value;
+    const char *vs = smem + OFF_V + SL * TB;
 #pragma unroll
     for (int c = 0; c < ND32; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int byte = c * 64 + 32 * (g & 1) + 8 * (s16 & 3);
-        const char *ap = vs + (kb * 16 + v_row) * RB + (((byte >> 4) ^ v_sw) << 4) + (byte & 15);
-        const u32x2 a0 = lds_read_tr4(ap);
-        const u32x2 a1 = lds_read_tr4(ap + 8 * RB);
+        const u32x2 a0 = lds_read_tr4(vs + kb * 16 * RB + v_addr[c][0]);
+        const u32x2 a1 = lds_read_tr4(vs + kb * 16 * RB + v_addr[c][1]);
         const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -271,27 +295,34 @@ void fwd_kernel(FwdParams p) {
     }
   };
 
-  // K(t + PREFETCH) and V(t + PREFETCH) are issued at step t
+  // K(t + 1) and V(t + 1) are issued at step t into the other slot
   auto issue_step = [&](int t) {
-    issue_tile(rk, t + PREFETCH, 0, dma_k_off);
-    issue_tile(rv, t + PREFETCH, OFF_V, dma_v_off);
+    issue_tile(rk, t + 1, 0, dma_k_off);
+    issue_tile(rv, t + 1, OFF_V, dma_v_off);
   };
-#pragma unroll
-  for (int t = -PREFETCH; t < 0; ++t) issue_step(t);
-  wait_vmcnt<DMA_PER_STEP * (PREFETCH - 1)>();
-  barrier_only();
-  for (int t = 0; t < nt; ++t) {
+  auto step = [&](int t, auto slot) {
     issue_step(t);
-    stage_s(t, sacc);
+    stage_s(slot, sacc);
     if (needs_mask(t)) apply_mask(t, sacc);
     float alpha[QB];
     const bool resc = stage_softmax(sacc, pk, alpha);
     if (__builtin_amdgcn_ballot_w64(resc) != 0) rescale_o(alpha);
-    stage_pv(t, pk);
-    // tiles used at step t+1 were issued PREFETCH-1 steps ago
-    wait_vmcnt<DMA_PER_STEP * (PREFETCH - 1)>();
+    stage_pv(slot, pk);
+    wait_vmcnt<0>();  // tiles for step t + 1 have landed
     barrier_only();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  issue_step(-1);
+  wait_vmcnt<0>();
+  barrier_only();
+  int t = 0;
+  for (; t + 1 < nt; t += 2) {  // tile t lives in slot t & 1
+    step(t, S0{});
+    step(t + 1, S1{});
   }
+  if (t < nt) step(t, S0{});
   wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
   // ---- epilogue: O = acc / l (rounded to 16 bits), LSE = (m + log2 l) ln 2
