@@ -133,7 +133,7 @@ int fa_bwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *pl
   plan->block_n = fa::BWD_DKDV_BN;
   plan->threads = 256;
   plan->grid = (int)(nk * B * H);
-  plan->lds_bytes = 2 * (2 * fa::BWD_DKDV_BM * d * 2 + 512);
+  plan->lds_bytes = BWD_DKDV_NSLOT * (2 * fa::BWD_DKDV_BM * d * 2 + fa::BWD_DKDV_STAT);
   plan->xcd_grouped = ((long long)B * H) % 8 == 0;
   return FA_OK;
 }

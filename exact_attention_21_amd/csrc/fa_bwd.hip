@@ -26,6 +26,8 @@
 // dK^T += Q^T dS, with dO^T and Q^T read transposed from LDS).  Tiles reach LDS
 // by direct buffer->LDS loads one step ahead, with XOR-swizzled rows (see the
 // forward kernel).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -42,9 +44,18 @@ __device__ __forceinline__ int swz_frag(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 template <int D>
-__device__ __forceinline__ int swz_both(int row) {
-  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row & 3) << 1) ^ (row >> 2)) & 7);
+__host__ __device__ constexpr int swz_both(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row & 3) << 1) ^ ((row >> 2) & 3)) & 7);
 }
+// Both swizzles repeat every 16 rows, so a fragment address precomputed for
+// rows r .. r + 15 serves rows r + 16 .. r + 31 with a constant offset.
+template <int D>
+constexpr bool swz_period16() {
+  for (int r = 0; r < 16; ++r)
+    if (swz_both<D>(r + 16) != swz_both<D>(r) || ((r + 16) & 15) != (r & 15)) return false;
+  return true;
+}
+static_assert(swz_period16<64>() && swz_period16<128>(), "swizzles must repeat every 16 rows");
 
 }  // namespace
 
@@ -256,17 +267,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DKDV_WA
 void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BM = BWD_DKDV_BM;       // query rows per step
   constexpr int BN = BWD_DKDV_BN;       // keys per workgroup (32 per wave)
+  constexpr int NS = BWD_DKDV_NSLOT;    // ring slots (loads run NS - 1 steps ahead)
   constexpr int RB = D * 2;
   constexpr int TB = BM * RB;           // bytes per Q (or dO) tile
-  constexpr int STAT = 512;             // LSE2 (64 floats read, 32 used), then D
+  constexpr int STAT = BWD_DKDV_STAT;   // LSE2 (64 floats read, 32 used), then D
   constexpr int SLOT = 2 * TB + STAT;   // Q, dO, stats
   constexpr int CPR = RB / 16;
   constexpr int ROWS_PER_BLOCK = 64 / CPR;
   constexpr int BPW = TB / 1024 / 4;
   constexpr int ND16 = D / 16, ND32 = D / 32;
-  static_assert(BPW >= 1 && BM == 32 && BN == 128, "tile shape");
+  static_assert(BPW >= 1 && BM == 32 && BN == 128 && NS >= 2 && NS <= 3, "tile shape");
+  // buffer->LDS loads a wave issues per step: Q and dO blocks, and (wave 0) the two stats rows
+  constexpr int DMA_W = 2 * BPW, DMA_W0 = 2 * BPW + 2;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT];
+  // one LDS object per ring slot, so that the compiler can tell a slot being
+  // loaded from the slot being read (it then needs no wait between the two)
+  __shared__ __attribute__((aligned(1024))) char slot0[SLOT];
+  __shared__ __attribute__((aligned(1024))) char slot1[SLOT];
+  __shared__ __attribute__((aligned(1024))) char slot2[NS == 3 ? SLOT : 16];
+  auto slot_base = [&](auto slot) -> char * {
+    constexpr int SL = decltype(slot)::value;
+    if constexpr (SL == 0) return slot0;
+    else if constexpr (SL == 1) return slot1;
+    else return slot2;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -321,22 +345,31 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int row = (w * BPW + j) * ROWS_PER_BLOCK + lane / CPR, pos = lane % CPR;
     dq_off[j] = (uint32_t)(row * RB + ((pos ^ swz_both<D>(row)) << 4));
   }
-  // step i loads query tile qt0 + i into slot i & 1: Q, dO (swizzled), LSE2, D
-  auto issue_step = [&](int i) {
+  // step i loads query tile qt0 + i into ring slot SL: Q, dO (swizzled), LSE2, D
+  auto issue_step = [&](int i, auto slot) {
+    constexpr int SL = decltype(slot)::value;
     const int qtile = qt0 + i;
     const bool ok = qtile < nqt;
     const uint32_t base = ok ? (uint32_t)qtile * TB : 0x80000000u;
-    char *slot = smem + (i & 1) * SLOT;
+    char *sp = slot_base(slot);
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
-      dma16(rq, slot + (w * BPW + j) * 1024, base + dq_off[j]);
-      dma16(rdo, slot + TB + (w * BPW + j) * 1024, base + dq_off[j]);
+      dma16(rq, sp + (w * BPW + j) * 1024, base + dq_off[j]);
+      dma16(rdo, sp + TB + (w * BPW + j) * 1024, base + dq_off[j]);
     }
     if (w == 0) {  // 64 lanes x 4 bytes each: rows qtile*BM + lane (the first 32 are used)
       const uint32_t so = ok ? (uint32_t)(qtile * BM + lane) * 4 : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void *)(slot + 2 * TB), 4, so, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void *)(slot + 2 * TB + 256), 4, so, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void *)(sp + 2 * TB), 4, so, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void *)(sp + 2 * TB + 256), 4, so, 0, 0, 0);
     }
+  };
+  // wait until at most `steps` steps of this wave's loads are in flight
+  auto wait_dma = [&](auto steps) {
+    constexpr int K = decltype(steps)::value;
+    if (w == 0)
+      wait_vmcnt<K * DMA_W0>();
+    else
+      wait_vmcnt<K * DMA_W>();
   };
 
   f32x16 dkacc[ND32], dvacc[ND32];
@@ -346,26 +379,41 @@ void bwd_dkdv_kernel(BwdParams p) {
     dvacc[c] = f32x16{};
   }
 
-  const int f_sw = swz_both<D>(l32);
-  const int t_row = 4 * (g >> 1) + (s16 >> 2);
+  // Fragment-read byte offsets inside a slot.  The 16-byte fragment of column
+  // block db sits at f_base ^ (32 db): the swizzle permutes whole 16-byte chunks
+  // of one row and 32 db only touches chunk bits.  Likewise the transposing
+  // reads of 32-column block c sit at t_base[h] ^ (64 c), and the second
+  // 16-row half of a tile at + 16 rows (the swizzles repeat every 16 rows).
+  uint32_t f_base = (uint32_t)(l32 * RB + ((hi ^ swz_both<D>(l32)) << 4));
+  uint32_t t_base[2];
+  {
+    const int t_row = 4 * (g >> 1) + (s16 >> 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = t_row + 8 * h;
+      const int byte = 32 * (g & 1) + 8 * (s16 & 3);
+      t_base[h] = (uint32_t)(row * RB + (((byte >> 4) ^ swz_both<D>(row)) << 4) + (byte & 15));
+    }
+  }
 
-  const int nsteps = nqt - qt0;
-  issue_step(0);
-  wait_vmcnt<0>();
-  barrier_only();
-  for (int i = 0; i < nsteps; ++i) {
-    issue_step(i + 1);
-    const char *qs = smem + (i & 1) * SLOT;
+  // one step on query tile qt0 + i held in ring slot SL
+  auto step = [&](int i, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    issue_step(i + NS - 1, std::integral_constant<int, (SL + NS - 1) % NS>{});
+    const char *qs = slot_base(slot);
     const char *ds = qs + TB;
     const float *ls = reinterpret_cast<const float *>(qs + 2 * TB);  // LSE2 at [0, 32), D at [64, 96)
     const int q0 = (qt0 + i) * BM;
+    // keep the per-block addresses out of the loop-invariant set: they are two
+    // cheap VALU ops each, registers are not
+    asm volatile("" : "+v"(f_base), "+v"(t_base[0]), "+v"(t_base[1]));
     // S = Q K^T and dP = dO V^T (queries x keys): lane = key, registers = queries
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int db = 0; db < ND16; ++db) {
-      const int off = l32 * RB + (((2 * db + hi) ^ f_sw) << 4);
-      s = T::mma(lds_read16(qs + off), kf[db], s);
-      dp = T::mma(lds_read16(ds + off), vf[db], dp);
+      const uint32_t fa = f_base ^ (uint32_t)(32 * db);
+      s = T::mma(lds_read16(qs + fa), kf[db], s);
+      dp = T::mma(lds_read16(ds + fa), vf[db], dp);
     }
     const bool need_mask = CAUSAL && q0 < kw0 + 31;
     uint32_t pk[8], sk[8];
@@ -394,21 +442,40 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int c = 0; c < ND32; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int byte = c * 64 + 32 * (g & 1) + 8 * (s16 & 3);
-        const int r0 = kb * 16 + t_row;
-        const int o0 = r0 * RB + (((byte >> 4) ^ swz_both<D>(r0)) << 4) + (byte & 15);
-        const int o1 = (r0 + 8) * RB + (((byte >> 4) ^ swz_both<D>(r0 + 8)) << 4) + (byte & 15);
-        const u32x2 d0 = lds_read_tr4(ds + o0), d1 = lds_read_tr4(ds + o1);
-        const u32x2 q0v = lds_read_tr4(qs + o0), q1v = lds_read_tr4(qs + o1);
+        const uint32_t ta0 = t_base[0] ^ (uint32_t)(64 * c), ta1 = t_base[1] ^ (uint32_t)(64 * c);
+        const u32x2 d0 = lds_read_tr4(ds + kb * 16 * RB + ta0);
+        const u32x2 d1 = lds_read_tr4(ds + kb * 16 * RB + ta1);
+        const u32x2 q0v = lds_read_tr4(qs + kb * 16 * RB + ta0);
+        const u32x2 q1v = lds_read_tr4(qs + kb * 16 * RB + ta1);
         const u32x4 bp = {pk[4 * kb], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
         const u32x4 bs = {sk[4 * kb], sk[4 * kb + 1], sk[4 * kb + 2], sk[4 * kb + 3]};
         dvacc[c] = T::mma(u32x4{d0[0], d0[1], d1[0], d1[1]}, bp, dvacc[c]);
         dkacc[c] = T::mma(u32x4{q0v[0], q0v[1], q1v[0], q1v[1]}, bs, dkacc[c]);
       }
     }
-    wait_vmcnt<0>();  // tiles for step i + 1 have landed
+    wait_dma(std::integral_constant<int, NS - 2>{});  // tiles for step i + 1 have landed
     barrier_only();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2 % NS>;
+
+  const int nsteps = nqt - qt0;
+  issue_step(0, S0{});
+  if constexpr (NS == 3) issue_step(1, S1{});
+  wait_dma(std::integral_constant<int, NS - 2>{});
+  barrier_only();
+  int i = 0;
+  for (; i + NS <= nsteps; i += NS) {  // query tile qt0 + i lives in slot i % NS
+    step(i, S0{});
+    step(i + 1, S1{});
+    if constexpr (NS == 3) step(i + 2, S2{});
   }
+  if (i < nsteps) step(i, S0{});
+  if constexpr (NS == 3) {
+    if (i + 1 < nsteps) step(i + 1, S1{});
+  }
+  wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
   // dK = scale dK^T^T, dV = dV^T^T, rounded to 16 bits
   if (key < N) {

@@ -44,6 +44,11 @@ constexpr int BWD_DKDV_BM = 32;
 #ifndef BWD_DKDV_WAVES_PER_SIMD
 #define BWD_DKDV_WAVES_PER_SIMD 2
 #endif
+// Ring slots of the dK/dV pass: Q/dO tiles are loaded NSLOT - 1 steps ahead.
+#ifndef BWD_DKDV_NSLOT
+#define BWD_DKDV_NSLOT 2
+#endif
+constexpr int BWD_DKDV_STAT = 512;  // bytes of LSE2 and D per ring slot
 
 struct BwdParams {
   const void *q, *k, *v, *o, *dout;
