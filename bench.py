@@ -14,9 +14,13 @@ kernels run on.  The CPU baseline times the fp64 oracle on a bounded sample of
 the same workload (one head: the forward over every row, the backward over the
 whole head) on the host's cores.
 
+After the headline step the other configurations of the workload family (the
+sequence-length sweep N = 1k..32k at 32768 tokens per batch, the d=64 variant,
+the non-causal 4096 forward, the 4096 backward) are timed too and reported under
+"sweep" (skip with --no-sweep; --sweep-only runs just those).
+
 Extra modes: --copy-ref MiB runs a plain device copy of known size (the
-reference for scaling hardware byte counters); --check compares a few sampled
-rows against the oracle.
+reference for scaling hardware byte counters); --fwd-only times the forward alone.
 """
 from __future__ import annotations
 
@@ -112,6 +116,52 @@ def cpu_baseline(bits, w, max_bwd_n):
             "sample": sample + f"; nominal FLOP {flop:.3e} in {secs:.1f} s"}
 
 
+def sweep(fa, device, steps, warmup):
+    """Forward and backward timings over the other configurations of the workload
+    family (sequence-length sweep at 32768 tokens per batch, the d=64 variant, the
+    non-causal 4096 forward and the 4096 backward).  Inputs are seeded N(0,1)
+    draws made on the device (timing only; parity is the tests' job)."""
+    import torch
+    import fa_inputs
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, c in fa_inputs.CONFIGS.items():
+        if name.startswith("c1_") or name.startswith("c3_"):
+            continue  # c1 is the oracle-sized case; c3 is the headline above
+        B, H, N, d, causal = c["B"], c["H"], c["N"], c["d"], c["causal"]
+        tdt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float16
+        gen = torch.Generator(device=device).manual_seed(c["seed"])
+        q, k, v, do = (torch.randn((B, H, N, d), generator=gen, device=device, dtype=torch.float32).to(tdt)
+                       for _ in range(4))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=device)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=device)
+        scale = 1 / math.sqrt(d)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(warmup + steps):
+            e = ev[i - warmup] if i >= warmup else None
+            if e:
+                e[0].record(stream)
+            fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
+            if e:
+                e[1].record(stream)
+            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, ws, stream)
+            if e:
+                e[2].record(stream)
+        torch.cuda.synchronize()
+        f_fwd, f_bwd = nominal_flop(B, H, N, d, causal)
+        fms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+        bms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+        res[name] = {"B": B, "H": H, "N": N, "d": d, "dtype": c["dtype"], "causal": causal,
+                     "fwd_ms": fms, "fwd_tflops": f_fwd / (fms * 1e-3) / 1e12,
+                     "bwd_ms": bms, "bwd_tflops": f_bwd / (bms * 1e-3) / 1e12}
+        log(f"[bench] sweep {name}: fwd {fms:.3f} ms ({res[name]['fwd_tflops']:.0f} TFLOP/s)  "
+            f"bwd {bms:.3f} ms ({res[name]['bwd_tflops']:.0f} TFLOP/s nominal)")
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+    return res
+
+
 def copy_ref(mib, device):
     import torch
     n = mib * (1 << 20)
@@ -134,6 +184,8 @@ def main():
                     help="largest N for which the CPU baseline includes the backward")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (diagnostics)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the other configurations' timings")
+    ap.add_argument("--sweep-only", action="store_true", help="time only the other configurations")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -150,6 +202,10 @@ def main():
     torch.cuda.set_device(device)
     if args.copy_ref:
         copy_ref(args.copy_ref, device)
+        return
+
+    if args.sweep_only:
+        print(json.dumps({"sweep": sweep(fa, device, args.steps, args.warmup)}), flush=True)
         return
 
     w = WORKLOAD
@@ -225,6 +281,11 @@ def main():
                    "frac_of_peak": (fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if fl else None}
                for n, (ms, fl) in kern.items()}
 
+    swp = None
+    if not args.no_sweep and not args.fwd_only:
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        swp = sweep(fa, device, max(3, args.steps // 2), 2)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
@@ -253,6 +314,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "sweep": swp,
     }
     print(json.dumps(out), flush=True)
 

@@ -104,14 +104,18 @@ void bwd_dq_kernel(BwdParams p) {
   constexpr int BM = BWD_DQ_BM;         // query rows per workgroup (32 per wave)
   constexpr int RB = D * 2;             // bytes per tile row
   constexpr int TB = BN * RB;           // bytes per K (or V) tile
-  constexpr int OFF_V = 2 * TB;         // K ring (2 slots), then V ring (2 slots)
   constexpr int CPR = RB / 16;
   constexpr int ROWS_PER_BLOCK = 64 / CPR;
   constexpr int BPW = TB / 1024 / 4;    // DMA blocks per wave per tile
   constexpr int ND16 = D / 16, ND32 = D / 32;
   static_assert(BPW >= 1 && BM == 128, "tile shape");
 
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
+  // two-slot K and V rings, one LDS object per slot (the compiler can then tell
+  // the slot being loaded from the slot being read)
+  __shared__ __attribute__((aligned(1024))) char k_slot0[TB];
+  __shared__ __attribute__((aligned(1024))) char k_slot1[TB];
+  __shared__ __attribute__((aligned(1024))) char v_slot0[TB];
+  __shared__ __attribute__((aligned(1024))) char v_slot1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,11 +174,13 @@ void bwd_dq_kernel(BwdParams p) {
     dk_off[j] = (uint32_t)(row * RB + ((pos ^ swz_both<D>(row)) << 4));
     dv_off[j] = (uint32_t)(row * RB + ((pos ^ swz_frag<D>(row)) << 4));
   }
-  auto issue_step = [&](int t) {  // tiles outside [0, nt) load as zeros
+  // tile t goes to ring slot SL (tiles outside [0, nt) load as zeros)
+  auto issue_step = [&](int t, auto slot) {
+    constexpr int SL = decltype(slot)::value;
     const bool ok = t >= 0 && t < nt;
     const uint32_t base = ok ? (uint32_t)t * TB : 0x80000000u;
-    char *ks = smem + (t & 1) * TB;
-    char *vs = smem + OFF_V + (t & 1) * TB;
+    char *ks = SL == 0 ? k_slot0 : k_slot1;
+    char *vs = SL == 0 ? v_slot0 : v_slot1;
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
       dma16(rk, ks + (w * BPW + j) * 1024, base + dk_off[j]);
@@ -186,28 +192,41 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int c = 0; c < ND32; ++c) dqacc[c] = f32x16{};
 
-  const int f_sw = swz_frag<D>(l32), b_sw = swz_both<D>(l32);
-  const int t_row = 4 * (g >> 1) + (s16 >> 2);
+  // Fragment-read byte offsets inside a slot: column block db of a K (V) row at
+  // kf_base (vf_base) ^ (32 db); transposing reads of 32-column block c at
+  // t_base[h] ^ (64 c), + 16 rows for the second half of the tile (the swizzles
+  // permute whole 16-byte chunks of a row and repeat every 16 rows).
+  uint32_t kf_base = (uint32_t)(l32 * RB + ((hi ^ swz_both<D>(l32)) << 4));
+  uint32_t vf_base = (uint32_t)(l32 * RB + ((hi ^ swz_frag<D>(l32)) << 4));
+  uint32_t t_base[2];
+  {
+    const int t_row = 4 * (g >> 1) + (s16 >> 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = t_row + 8 * h;
+      const int byte = 32 * (g & 1) + 8 * (s16 & 3);
+      t_base[h] = (uint32_t)(row * RB + (((byte >> 4) ^ swz_both<D>(row)) << 4) + (byte & 15));
+    }
+  }
+  const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
 
-  issue_step(0);
-  wait_vmcnt<0>();
-  barrier_only();
-  for (int t = 0; t < nt; ++t) {
-    issue_step(t + 1);
-    const char *ks = smem + (t & 1) * TB;
-    const char *vs = smem + OFF_V + (t & 1) * TB;
+  // one step on key tile t held in ring slot SL
+  auto step = [&](int t, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    issue_step(t + 1, std::integral_constant<int, SL ^ 1>{});
+    const char *ks = SL == 0 ? k_slot0 : k_slot1;
+    const char *vs = SL == 0 ? v_slot0 : v_slot1;
+    asm volatile("" : "+v"(kf_base), "+v"(vf_base), "+v"(t_base[0]), "+v"(t_base[1]));
     // S^T = K Q^T and dP^T = V dO^T (keys x queries)
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int db = 0; db < ND16; ++db) {
-      const int ch = 2 * db + hi;
-      s = T::mma(lds_read16(ks + l32 * RB + ((ch ^ b_sw) << 4)), qf[db], s);
-      dp = T::mma(lds_read16(vs + l32 * RB + ((ch ^ f_sw) << 4)), dof[db], dp);
+      s = T::mma(lds_read16(ks + (kf_base ^ (uint32_t)(32 * db))), qf[db], s);
+      dp = T::mma(lds_read16(vs + (vf_base ^ (uint32_t)(32 * db))), dof[db], dp);
     }
     // P^T = exp2(scale log2e S - LSE log2e), masked; dS^T = P^T (dP^T - D)
     const int j0 = t * BN;
     const bool need_mask = (CAUSAL && j0 + BN - 1 > wr0) || (j0 + BN > N);
-    const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
     uint32_t dsk[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -229,18 +248,29 @@ void bwd_dq_kernel(BwdParams p) {
     for (int c = 0; c < ND32; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int byte = c * 64 + 32 * (g & 1) + 8 * (s16 & 3);
-        const int r0 = kb * 16 + t_row;
-        const char *ap0 = ks + r0 * RB + (((byte >> 4) ^ swz_both<D>(r0)) << 4) + (byte & 15);
-        const char *ap1 = ks + (r0 + 8) * RB + (((byte >> 4) ^ swz_both<D>(r0 + 8)) << 4) + (byte & 15);
-        const u32x2 a0 = lds_read_tr4(ap0), a1 = lds_read_tr4(ap1);
+        const char *kk = ks + kb * 16 * RB;
+        const u32x2 a0 = lds_read_tr4(kk + (t_base[0] ^ (uint32_t)(64 * c)));
+        const u32x2 a1 = lds_read_tr4(kk + (t_base[1] ^ (uint32_t)(64 * c)));
         const u32x4 b = {dsk[4 * kb], dsk[4 * kb + 1], dsk[4 * kb + 2], dsk[4 * kb + 3]};
         dqacc[c] = T::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, b, dqacc[c]);
       }
     }
     wait_vmcnt<0>();  // tiles for step t + 1 have landed
     barrier_only();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  issue_step(0, S0{});
+  wait_vmcnt<0>();
+  barrier_only();
+  int t = 0;
+  for (; t + 1 < nt; t += 2) {  // key tile t lives in slot t & 1
+    step(t, S0{});
+    step(t + 1, S1{});
   }
+  if (t < nt) step(t, S0{});
+  wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
   // dQ = scale dQ^T^T, rounded to 16 bits
   if (qrow < N) {

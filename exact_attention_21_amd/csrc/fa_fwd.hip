@@ -83,24 +83,31 @@ static_assert(swz_v_period16<64>() && swz_v_period16<128>(), "V swizzle must rep
 
 }  // namespace
 
+// waves per SIMD: two query blocks per wave need the registers of occupancy 2
+#define FWD_OCC(D, QB) ((QB) == 2 ? 2 : (D) == 64 ? FWD_WAVES_D64 : FWD_WAVES_PER_SIMD)
+
 template <class T, int D, int QB, bool CAUSAL, bool O_IN_AGPR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_SIMD, FWD_WAVES_PER_SIMD)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FWD_OCC(D, QB), FWD_OCC(D, QB))))
 void fwd_kernel(FwdParams p) {
   constexpr int BN = FWD_BN;
   constexpr int BM = 128 * QB;          // query rows per workgroup
   constexpr int WR = 32 * QB;           // query rows per wave
   constexpr int RB = D * 2;             // bytes per tile row (unpadded)
   constexpr int TB = BN * RB;           // bytes of one K (or V) tile
-  constexpr int OFF_V = NSLOT * TB;     // K ring, then V ring
   constexpr int CPR = RB / 16;          // 16-byte chunks per row
   constexpr int ROWS_PER_BLOCK = 64 / CPR;       // rows covered by one 1 KB DMA block
   constexpr int BLOCKS = TB / 1024;              // DMA blocks per tile
   constexpr int BPW = BLOCKS / 4;                // DMA blocks per wave per tile
-  constexpr int DMA_PER_STEP = 2 * BPW;          // K + V loads issued per wave per step
   constexpr int ND16 = D / 16, ND32 = D / 32;
   static_assert(BLOCKS % 4 == 0, "tile must split evenly over 4 waves");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NSLOT * TB];
+  // K and V rings of NSLOT = 2 slots, one LDS object per slot (the compiler can
+  // then tell the slot being loaded from the slot being read)
+  static_assert(NSLOT == 2, "two-slot rings");
+  __shared__ __attribute__((aligned(1024))) char k_slot0[TB];
+  __shared__ __attribute__((aligned(1024))) char k_slot1[TB];
+  __shared__ __attribute__((aligned(1024))) char v_slot0[TB];
+  __shared__ __attribute__((aligned(1024))) char v_slot1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -146,12 +153,11 @@ void fwd_kernel(FwdParams p) {
     dma_k_off[j] = (uint32_t)(row * RB + ((pos ^ swz_k<D>(row)) << 4));
     dma_v_off[j] = (uint32_t)(row * RB + ((pos ^ swz_v<D>(row)) << 4));
   }
-  auto issue_tile = [&](const __amdgpu_buffer_rsrc_t &rsrc, int t, int ring_off,
+  auto issue_tile = [&](const __amdgpu_buffer_rsrc_t &rsrc, int t, char *slot,
                         const uint32_t (&offs)[BPW]) {
     // tiles outside [0, nt) load as zeros (offset past the resource end)
     const bool ok = t >= 0 && t < nt;
     const uint32_t base = ok ? (uint32_t)t * TB : 0x80000000u;
-    char *slot = smem + ring_off + ((t + NSLOT) % NSLOT) * TB;
 #pragma unroll
     for (int j = 0; j < BPW; ++j) dma16(rsrc, slot + (w * BPW + j) * 1024, base + offs[j]);
   };
@@ -203,7 +209,7 @@ void fwd_kernel(FwdParams p) {
   // S(t) = K(t) Q^T, K(t) in ring slot SL
   auto stage_s = [&](auto slot, f32x16 (&s)[QB]) {
     constexpr int SL = decltype(slot)::value;
-    const char *ks = smem + SL * TB;
+    const char *ks = SL == 0 ? k_slot0 : k_slot1;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
@@ -263,7 +269,7 @@ void fwd_kernel(FwdParams p) {
   // O^T += V(t)^T P(t)^T, V(t) in ring slot SL
   auto stage_pv = [&](auto slot, const uint32_t (&pk)[QB][8]) {
     constexpr int SL = decltype(slot)::value;
-    const char *vs = smem + OFF_V + SL * TB;
+    const char *vs = SL == 0 ? v_slot0 : v_slot1;
 #pragma unroll
     for (int c = 0; c < ND32; ++c) {
 #pragma unroll
@@ -295,13 +301,16 @@ void fwd_kernel(FwdParams p) {
     }
   };
 
-  // K(t + 1) and V(t + 1) are issued at step t into the other slot
-  auto issue_step = [&](int t) {
-    issue_tile(rk, t + 1, 0, dma_k_off);
-    issue_tile(rv, t + 1, OFF_V, dma_v_off);
+  // K(t) and V(t) go to ring slot SL
+  auto issue_step = [&](int t, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    issue_tile(rk, t, SL == 0 ? k_slot0 : k_slot1, dma_k_off);
+    issue_tile(rv, t, SL == 0 ? v_slot0 : v_slot1, dma_v_off);
   };
+  // one step on tile t held in slot SL; tile t + 1 is loaded into the other slot
   auto step = [&](int t, auto slot) {
-    issue_step(t);
+    constexpr int SL = decltype(slot)::value;
+    issue_step(t + 1, std::integral_constant<int, SL ^ 1>{});
     stage_s(slot, sacc);
     if (needs_mask(t)) apply_mask(t, sacc);
     float alpha[QB];
@@ -314,7 +323,7 @@ void fwd_kernel(FwdParams p) {
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
-  issue_step(-1);
+  issue_step(0, S0{});
   wait_vmcnt<0>();
   barrier_only();
   int t = 0;

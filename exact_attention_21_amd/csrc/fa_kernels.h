@@ -22,6 +22,13 @@ constexpr int FWD_BN = 32;
 #ifndef FWD_WAVES_PER_SIMD
 #define FWD_WAVES_PER_SIMD 3
 #endif
+// d = 64: query blocks per wave for N > 128, and the occupancy of the one-block kernel
+#ifndef FWD_QB_D64
+#define FWD_QB_D64 2
+#endif
+#ifndef FWD_WAVES_D64
+#define FWD_WAVES_D64 3
+#endif
 
 struct FwdParams {
   const void *q, *k, *v;
