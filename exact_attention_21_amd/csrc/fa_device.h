@@ -131,10 +131,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Workgroup barrier without the memory fences of __syncthreads (which would
-// also drain every outstanding global load); the memory clobber keeps the
-// compiler from moving LDS accesses across it.  Callers wait for the LDS
-// traffic that must be visible before calling it.
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+// also drain every outstanding global load).  It first waits for this wave's
+// own LDS reads: the compiler may sink the arithmetic that consumes a read
+// below the barrier, and the read must not still be in flight when another
+// wave passes the barrier and starts overwriting that LDS.  The memory clobber
+// keeps the compiler from moving LDS accesses across it.  Callers wait (vmcnt)
+// for the buffer->LDS loads that must have landed before calling it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }   // v_log_f32 (base 2)
