@@ -10,6 +10,10 @@ Functions:
   fwd_rows(q, k, v, scale, causal, rows) -> (o, lse)   selected flat rows b*H*N+h*N+i
   bwd(q, k, v, dout, scale, causal)      -> (dq, dk, dv)
   bwd_heads(q, k, v, dout, scale, causal, heads) -> (dq, dk, dv) for heads b*H+h
+  fwd_padded(q, k, v, scale, causal, lq, lk)        -> (o, lse)
+  bwd_padded(q, k, v, dout, scale, causal, lq, lk)  -> (dq, dk, dv)
+      q, dout [B, H, Nq, d]; k, v [B, H, Nk, d]; lq, lk per-batch valid lengths
+      (None = all valid); causal is aligned to the last query and key.
 Inputs are float64 arrays [B, H, N, d] (exactly widened 16-bit values).
 """
 from __future__ import annotations
@@ -52,6 +56,10 @@ def _load():
         lib.oracle_bwd_heads.restype = I
         lib.oracle_bwd.argtypes = [dp, dp, dp, dp, L, L, L, L, D, I, dp, dp, dp, I]
         lib.oracle_bwd.restype = I
+        lib.oracle_fwd_padded.argtypes = [dp, dp, dp, L, L, L, L, L, lp, lp, D, I, dp, dp]
+        lib.oracle_fwd_padded.restype = I
+        lib.oracle_bwd_padded.argtypes = [dp, dp, dp, dp, L, L, L, L, L, lp, lp, D, I, dp, dp, dp, I]
+        lib.oracle_bwd_padded.restype = I
         _lib = lib
     return _lib
 
@@ -125,4 +133,49 @@ def bwd(q, k, v, dout, scale: float, causal: bool, threads: int | None = None):
                             _p(dq), _p(dk), _p(dv), threads or default_threads())
     if rc:
         raise RuntimeError(f"oracle_bwd failed ({rc})")
+    return dq, dk, dv
+
+
+def _lens(x, B):
+    if x is None:
+        return None, None
+    a = np.ascontiguousarray(x, dtype=np.int64).ravel()
+    if a.size != B:
+        raise ValueError("one length per batch entry")
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_long))
+
+
+def fwd_padded(q, k, v, scale: float, causal: bool, lq=None, lk=None):
+    q, k, v = _as4(q), _as4(k), _as4(v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k, v must be [B, H, Nk, d]")
+    lqa, lqp = _lens(lq, B)
+    lka, lkp = _lens(lk, B)
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Nq), np.float64)
+    rc = _load().oracle_fwd_padded(_p(q), _p(k), _p(v), B, H, Nq, Nk, d, lqp, lkp, float(scale),
+                                   int(bool(causal)), _p(o), _p(lse))
+    if rc:
+        raise RuntimeError(f"oracle_fwd_padded failed ({rc})")
+    return o, lse
+
+
+def bwd_padded(q, k, v, dout, scale: float, causal: bool, lq=None, lk=None, threads: int | None = None):
+    q, k, v, dout = _as4(q), _as4(k), _as4(v), _as4(dout)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("k, v must be [B, H, Nk, d] and dout like q")
+    lqa, lqp = _lens(lq, B)
+    lka, lkp = _lens(lk, B)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(k)
+    rc = _load().oracle_bwd_padded(_p(q), _p(k), _p(v), _p(dout), B, H, Nq, Nk, d, lqp, lkp,
+                                   float(scale), int(bool(causal)), _p(dq), _p(dk), _p(dv),
+                                   threads or default_threads())
+    if rc:
+        raise RuntimeError(f"oracle_bwd_padded failed ({rc})")
     return dq, dk, dv

@@ -35,6 +35,17 @@
  * LSE is [B][H][N].  Rows of one head are split across pthreads; each row's full
  * score vector is formed (a row of the N x N matrix), so the result does not
  * depend on the thread count.
+ *
+ * Padded batches and cross-attention (oracle_fwd_padded, oracle_bwd_padded):
+ * Q, O, dO, dQ are [B][H][Nq][d], K, V, dK, dV are [B][H][Nk][d], and batch b
+ * has Lq[b] <= Nq valid queries and Lk[b] <= Nk valid keys (the padding mask
+ * that "Flash Attention application" (jsqmd.com), section "Notes", recommends
+ * beside the causal one; cross-attention with its own key length is the case
+ * llmtrend.com's "Limitations" section says needs a separate implementation).
+ * Valid query i sees valid key j iff !causal or j <= i + Lk - Lq: the causal
+ * diagonal is aligned to the last query and the last key, which for Lq = Lk is
+ * the square rule above.  A row with no visible key and every padding row has
+ * O = 0 and LSE = -inf and contributes nothing to the gradients.
  */
 #include <math.h>
 #include <pthread.h>
@@ -47,12 +58,24 @@
 /* forward                                                                    */
 /* ------------------------------------------------------------------------ */
 
-/* One query row: s_j = scale * q.k_j for visible j, P = softmax(s), o = P V,
- * lse = m + log(sum exp(s - m)).  `s` is scratch of length N. */
-static void fwd_row(const double *q, const double *K, const double *V, long N,
-                    long d, double scale, int causal, long i, double *o,
-                    double *lse, double *s) {
-  long nvis = causal ? i + 1 : N; /* keys 0..nvis-1 are visible */
+/* Number of keys visible to query i: keys 0 .. nvis-1 (see the header). */
+static long visible_keys(long i, long Lq, long Lk, int causal) {
+  if (i >= Lq) return 0; /* padding row */
+  if (!causal) return Lk;
+  long n = i + Lk - Lq + 1;
+  return n < 0 ? 0 : (n > Lk ? Lk : n);
+}
+
+/* One query row over its visible keys 0..nvis-1: s_j = scale * q.k_j,
+ * P = softmax(s), o = P V, lse = m + log(sum exp(s - m)); a row with no
+ * visible key gets o = 0, lse = -inf.  `s` is scratch of length nvis. */
+static void fwd_row(const double *q, const double *K, const double *V, long nvis,
+                    long d, double scale, double *o, double *lse, double *s) {
+  if (nvis == 0) {
+    for (long c = 0; c < d; ++c) o[c] = 0.0;
+    *lse = -INFINITY;
+    return;
+  }
   double m = -INFINITY;
   for (long j = 0; j < nvis; ++j) {
     double acc = 0.0;
@@ -93,8 +116,8 @@ static void *fwd_worker(void *arg) {
     long bh = flat / J->N, i = flat % J->N;
     const double *Kh = J->k + bh * J->N * J->d;
     const double *Vh = J->v + bh * J->N * J->d;
-    fwd_row(J->q + flat * J->d, Kh, Vh, J->N, J->d, J->scale, J->causal, i,
-            J->o + r * J->d, J->lse + r, s);
+    fwd_row(J->q + flat * J->d, Kh, Vh, visible_keys(i, J->N, J->N, J->causal), J->d,
+            J->scale, J->o + r * J->d, J->lse + r, s);
   }
   free(s);
   return NULL;
@@ -159,10 +182,12 @@ int oracle_fwd(const double *q, const double *k, const double *v, long B,
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
-  const double *q, *k, *v, *dout; /* this head, [N][d] */
-  double *P, *dS;                 /* [N][N] */
-  double *dq, *dk, *dv;           /* this head, [N][d] */
-  long N, d;
+  const double *q, *dout;         /* this head, [Nq][d] */
+  const double *k, *v;            /* this head, [Nk][d] */
+  double *P, *dS;                 /* [Nq][Nk] */
+  double *dq;                     /* this head, [Nq][d] */
+  double *dk, *dv;                /* this head, [Nk][d] */
+  long Nq, Nk, Lq, Lk, d;         /* Lq, Lk: valid queries / keys of this batch entry */
   double scale;
   int causal;
   int phase;
@@ -171,12 +196,12 @@ typedef struct {
 
 static void *bwd_worker(void *arg) {
   bwd_job *J = (bwd_job *)arg;
-  long N = J->N, d = J->d;
+  long Nq = J->Nq, Nk = J->Nk, d = J->d;
   if (J->phase == 0) {
     /* rows of P: recomputed from Q, K as in the forward */
     for (long i = J->a0; i < J->a1; ++i) {
-      double *Pi = J->P + i * N;
-      long nvis = J->causal ? i + 1 : N;
+      double *Pi = J->P + i * Nk;
+      long nvis = visible_keys(i, J->Lq, J->Lk, J->causal);
       double m = -INFINITY;
       for (long j = 0; j < nvis; ++j) {
         double acc = 0.0;
@@ -190,33 +215,33 @@ static void *bwd_worker(void *arg) {
         l += Pi[j];
       }
       for (long j = 0; j < nvis; ++j) Pi[j] /= l;
-      for (long j = nvis; j < N; ++j) Pi[j] = 0.0; /* masked: weight 0 */
+      for (long j = nvis; j < Nk; ++j) Pi[j] = 0.0; /* masked: weight 0 */
     }
   } else if (J->phase == 1) {
     /* dV_j = sum_i P_ij dO_i */
     for (long j = J->a0; j < J->a1; ++j)
       for (long c = 0; c < d; ++c) {
         double acc = 0.0;
-        for (long i = 0; i < N; ++i) acc += J->P[i * N + j] * J->dout[i * d + c];
+        for (long i = 0; i < Nq; ++i) acc += J->P[i * Nk + j] * J->dout[i * d + c];
         J->dv[j * d + c] = acc;
       }
   } else if (J->phase == 2) {
     /* dP_ij = dO_i . V_j ; D_i = sum_j P_ij dP_ij ; dS = P (dP - D) ;
      * dQ_i = scale * sum_j dS_ij K_j */
     for (long i = J->a0; i < J->a1; ++i) {
-      double *dSi = J->dS + i * N;
-      const double *Pi = J->P + i * N;
-      for (long j = 0; j < N; ++j) {
+      double *dSi = J->dS + i * Nk;
+      const double *Pi = J->P + i * Nk;
+      for (long j = 0; j < Nk; ++j) {
         double acc = 0.0;
         for (long c = 0; c < d; ++c) acc += J->dout[i * d + c] * J->v[j * d + c];
         dSi[j] = acc; /* dP for now */
       }
       double D = 0.0;
-      for (long j = 0; j < N; ++j) D += Pi[j] * dSi[j];
-      for (long j = 0; j < N; ++j) dSi[j] = Pi[j] * (dSi[j] - D);
+      for (long j = 0; j < Nk; ++j) D += Pi[j] * dSi[j];
+      for (long j = 0; j < Nk; ++j) dSi[j] = Pi[j] * (dSi[j] - D);
       for (long c = 0; c < d; ++c) {
         double acc = 0.0;
-        for (long j = 0; j < N; ++j) acc += dSi[j] * J->k[j * d + c];
+        for (long j = 0; j < Nk; ++j) acc += dSi[j] * J->k[j * d + c];
         J->dq[i * d + c] = J->scale * acc;
       }
     }
@@ -225,7 +250,7 @@ static void *bwd_worker(void *arg) {
     for (long j = J->a0; j < J->a1; ++j)
       for (long c = 0; c < d; ++c) {
         double acc = 0.0;
-        for (long i = 0; i < N; ++i) acc += J->dS[i * N + j] * J->q[i * d + c];
+        for (long i = 0; i < Nq; ++i) acc += J->dS[i * Nk + j] * J->q[i * d + c];
         J->dk[j * d + c] = J->scale * acc;
       }
   }
@@ -236,12 +261,12 @@ static int run_phase(bwd_job *base, int phase, int T) {
   pthread_t th[ORACLE_MAX_THREADS];
   bwd_job jobs[ORACLE_MAX_THREADS];
   int err = 0;
-  long N = base->N;
+  long n = (phase == 0 || phase == 2) ? base->Nq : base->Nk; /* rows or columns */
   for (int t = 0; t < T; ++t) {
     jobs[t] = *base;
     jobs[t].phase = phase;
-    jobs[t].a0 = N * t / T;
-    jobs[t].a1 = N * (t + 1) / T;
+    jobs[t].a0 = n * t / T;
+    jobs[t].a1 = n * (t + 1) / T;
   }
   for (int t = 1; t < T; ++t)
     if (pthread_create(&th[t], NULL, bwd_worker, &jobs[t])) err = 4;
@@ -279,7 +304,8 @@ int oracle_bwd_heads(const double *q, const double *k, const double *v,
     base.q = q + off; base.k = k + off; base.v = v + off; base.dout = dout + off;
     base.P = P; base.dS = dS;
     base.dq = dq + x * N * d; base.dk = dk + x * N * d; base.dv = dv + x * N * d;
-    base.N = N; base.d = d; base.scale = scale; base.causal = causal;
+    base.Nq = N; base.Nk = N; base.Lq = N; base.Lk = N;
+    base.d = d; base.scale = scale; base.causal = causal;
     for (int phase = 0; phase < 4 && !err; ++phase) err = run_phase(&base, phase, T);
   }
   free(P);
@@ -300,4 +326,77 @@ int oracle_bwd(const double *q, const double *k, const double *v,
                             dq, dk, dv, nthreads);
   free(heads);
   return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* padded batches and cross-attention (see the header)                        */
+/* ------------------------------------------------------------------------ */
+
+/* Lengths: lq[b] in [0, Nq], lk[b] in [0, Nk]; NULL means all valid. */
+static int lengths_ok(const long *lq, const long *lk, long B, long Nq, long Nk) {
+  for (long b = 0; b < B; ++b) {
+    if (lq && (lq[b] < 0 || lq[b] > Nq)) return 0;
+    if (lk && (lk[b] < 0 || lk[b] > Nk)) return 0;
+  }
+  return 1;
+}
+
+/* Forward over every row: o [B][H][Nq][d], lse [B][H][Nq]. */
+int oracle_fwd_padded(const double *q, const double *k, const double *v, long B,
+                      long H, long Nq, long Nk, long d, const long *lq,
+                      const long *lk, double scale, int causal, double *o,
+                      double *lse) {
+  if (!q || !k || !v || !o || !lse) return 1;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return 2;
+  if (!lengths_ok(lq, lk, B, Nq, Nk)) return 3;
+  double *s = (double *)malloc(sizeof(double) * (size_t)Nk);
+  if (!s) return 5;
+  for (long b = 0; b < B; ++b) {
+    long Lq = lq ? lq[b] : Nq, Lk = lk ? lk[b] : Nk;
+    for (long h = 0; h < H; ++h) {
+      long bh = b * H + h;
+      for (long i = 0; i < Nq; ++i)
+        fwd_row(q + (bh * Nq + i) * d, k + bh * Nk * d, v + bh * Nk * d,
+                visible_keys(i, Lq, Lk, causal), d, scale, o + (bh * Nq + i) * d,
+                lse + bh * Nq + i, s);
+    }
+  }
+  free(s);
+  return 0;
+}
+
+/* Backward over every head: dq [B][H][Nq][d], dk and dv [B][H][Nk][d]. */
+int oracle_bwd_padded(const double *q, const double *k, const double *v,
+                      const double *dout, long B, long H, long Nq, long Nk, long d,
+                      const long *lq, const long *lk, double scale, int causal,
+                      double *dq, double *dk, double *dv, int nthreads) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return 2;
+  if (!lengths_ok(lq, lk, B, Nq, Nk)) return 3;
+  int T = clamp_threads(nthreads);
+  if (T > Nq) T = (int)Nq;
+  if (T > Nk) T = (int)Nk;
+  double *P = (double *)malloc(sizeof(double) * (size_t)Nq * (size_t)Nk);
+  double *dS = (double *)malloc(sizeof(double) * (size_t)Nq * (size_t)Nk);
+  if (!P || !dS) {
+    free(P);
+    free(dS);
+    return 5;
+  }
+  int err = 0;
+  for (long bh = 0; bh < B * H && !err; ++bh) {
+    long b = bh / H;
+    bwd_job base;
+    memset(&base, 0, sizeof base);
+    base.q = q + bh * Nq * d; base.dout = dout + bh * Nq * d;
+    base.k = k + bh * Nk * d; base.v = v + bh * Nk * d;
+    base.P = P; base.dS = dS;
+    base.dq = dq + bh * Nq * d; base.dk = dk + bh * Nk * d; base.dv = dv + bh * Nk * d;
+    base.Nq = Nq; base.Nk = Nk; base.Lq = lq ? lq[b] : Nq; base.Lk = lk ? lk[b] : Nk;
+    base.d = d; base.scale = scale; base.causal = causal;
+    for (int phase = 0; phase < 4 && !err; ++phase) err = run_phase(&base, phase, T);
+  }
+  free(P);
+  free(dS);
+  return err;
 }

@@ -308,3 +308,160 @@ def test_bad_arguments_are_rejected():
         oracle.fwd_rows(q, q, q, 1.0, False, [4])
     with pytest.raises(RuntimeError):
         oracle.bwd_heads(q, q, q, q, 1.0, False, [1])
+
+
+# --------------------------------------------------------------------------
+# padded batches and cross-attention: per-batch valid lengths Lq <= Nq,
+# Lk <= Nk, causal aligned to the last query and key (oracle.fwd_padded /
+# oracle.bwd_padded)
+# --------------------------------------------------------------------------
+
+def visible_mask(Nq, Nk, Lq, Lk, causal):
+    """[Nq, Nk] bool: query i sees key j (the definition, written as a mask)."""
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    m = (i < Lq) & (j < Lk)
+    if causal:
+        m &= j <= i + (Lk - Lq)
+    return m
+
+
+def torch_padded_reference(q, k, v, dout, scale, causal, lq, lk):
+    """torch fp64 (library softmax, logsumexp, matmul, autograd) with an explicit
+    mask; rows that see no key get O = 0 and LSE = -inf and no gradient."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    Q, K, V = t(q), t(k), t(v)
+    mask = torch.stack([torch.from_numpy(visible_mask(Nq, Nk, lq[b], lk[b], causal)) for b in range(B)])
+    mask = mask[:, None]                                   # [B, 1, Nq, Nk]
+    rowvalid = mask.any(-1, keepdim=True)                  # [B, 1, Nq, 1]
+    s = torch.matmul(Q, K.transpose(-1, -2).contiguous()) * scale
+    s = s.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    s_safe = torch.where(rowvalid, s, torch.zeros_like(s))
+    p = torch.softmax(s_safe, dim=-1) * rowvalid
+    o = torch.matmul(p, V)
+    o.backward(torch.tensor(dout, dtype=torch.float64))
+    return o.detach().numpy(), lse.detach().numpy(), Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+
+
+PADDED_CASES = [
+    # Nq, Nk, lq, lk
+    (29, 41, [29, 17, 0], [41, 5, 30]),
+    (40, 13, [40, 33, 12], [13, 13, 0]),
+    (16, 16, [16, 9, 3], [16, 12, 16]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PADDED_CASES)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_padded_matches_torch_masked_reference(case, causal):
+    Nq, Nk, lq, lk = PADDED_CASES[case]
+    B, H, d = 3, 2, 8
+    q, do = rnd((B, H, Nq, d), 200 + case), rnd((B, H, Nq, d), 210 + case)
+    k, v = rnd((B, H, Nk, d), 220 + case), rnd((B, H, Nk, d), 230 + case)
+    scale = 0.4
+    o, lse = oracle.fwd_padded(q, k, v, scale, causal, lq, lk)
+    dq, dk, dv = oracle.bwd_padded(q, k, v, do, scale, causal, lq, lk)
+    to, tl, tdq, tdk, tdv = torch_padded_reference(q, k, v, do, scale, causal, lq, lk)
+    np.testing.assert_allclose(o, to, atol=1e-12)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(tl))
+    fin = np.isfinite(tl)
+    np.testing.assert_allclose(lse[fin], tl[fin], atol=1e-12)
+    np.testing.assert_allclose(dq, tdq, atol=1e-12)
+    np.testing.assert_allclose(dk, tdk, atol=1e-12)
+    np.testing.assert_allclose(dv, tdv, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_padded_full_lengths_equal_square_oracle(causal):
+    q, k, v, do = (rnd((2, 2, 37, 8), 240 + i) for i in range(4))
+    o, lse = oracle.fwd(q, k, v, 0.3, causal)
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.3, causal)
+    for lens in (None, [37, 37]):
+        po, pl = oracle.fwd_padded(q, k, v, 0.3, causal, lens, lens)
+        pq, pk, pv = oracle.bwd_padded(q, k, v, do, 0.3, causal, lens, lens)
+        assert np.array_equal(po, o) and np.array_equal(pl, lse)
+        assert np.array_equal(pq, dq) and np.array_equal(pk, dk) and np.array_equal(pv, dv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_padding_contents_do_not_matter(causal):
+    B, H, Nq, Nk, d = 2, 2, 19, 23, 4
+    lq, lk = [11, 19], [23, 7]
+    q, do = rnd((B, H, Nq, d), 250), rnd((B, H, Nq, d), 251)
+    k, v = rnd((B, H, Nk, d), 252), rnd((B, H, Nk, d), 253)
+    o, lse = oracle.fwd_padded(q, k, v, 0.5, causal, lq, lk)
+    dq, dk, dv = oracle.bwd_padded(q, k, v, do, 0.5, causal, lq, lk)
+    q2, do2, k2, v2 = q.copy(), do.copy(), k.copy(), v.copy()
+    for b in range(B):
+        q2[b, :, lq[b]:] = 1e3
+        do2[b, :, lq[b]:] = -7.0
+        k2[b, :, lk[b]:] = 1e3
+        v2[b, :, lk[b]:] = 5.0
+    o2, lse2 = oracle.fwd_padded(q2, k2, v2, 0.5, causal, lq, lk)
+    dq2, dk2, dv2 = oracle.bwd_padded(q2, k2, v2, do2, 0.5, causal, lq, lk)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    assert np.array_equal(dq, dq2) and np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+    for b in range(B):
+        assert np.all(o[b, :, lq[b]:] == 0) and np.all(np.isneginf(lse[b, :, lq[b]:]))
+        assert np.all(dq[b, :, lq[b]:] == 0)
+        assert np.all(dk[b, :, lk[b]:] == 0) and np.all(dv[b, :, lk[b]:] == 0)
+
+
+def test_bottom_right_causal_closed_forms():
+    # identical keys: query i of a causal cross-attention with Lk > Lq averages
+    # the first i + Lk - Lq + 1 values; with Lk < Lq the first Lq - Lk rows see nothing
+    d = 3
+    for Lq, Lk in ((4, 9), (9, 4), (1, 6)):
+        q = rnd((1, 1, Lq, d), 260)
+        k = np.tile(rnd((1, 1, 1, d), 261), (1, 1, Lk, 1))
+        v = rnd((1, 1, Lk, d), 262)
+        o, lse = oracle.fwd_padded(q, k, v, 0.7, True)
+        for i in range(Lq):
+            n = i + Lk - Lq + 1
+            if n <= 0:
+                assert np.all(o[0, 0, i] == 0) and np.isneginf(lse[0, 0, i])
+            else:
+                s = 0.7 * float(q[0, 0, i] @ k[0, 0, 0])
+                np.testing.assert_allclose(o[0, 0, i], v[0, 0, :n].mean(0), atol=1e-13)
+                np.testing.assert_allclose(lse[0, 0, i], s + math.log(n), atol=1e-13)
+    # a single query sees every key (it is the last query), causal or not
+    q, k, v = rnd((1, 2, 1, 5), 263), rnd((1, 2, 7, 5), 264), rnd((1, 2, 7, 5), 265)
+    a = oracle.fwd_padded(q, k, v, 0.4, True)
+    b = oracle.fwd_padded(q, k, v, 0.4, False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_padded_backward_central_differences(causal):
+    Nq, Nk, d = 4, 6, 3
+    lq, lk = [3], [5]
+    q, do = rnd((1, 1, Nq, d), 270), rnd((1, 1, Nq, d), 271)
+    k, v = rnd((1, 1, Nk, d), 272), rnd((1, 1, Nk, d), 273)
+    scale = 0.6
+    dq, dk, dv = oracle.bwd_padded(q, k, v, do, scale, causal, lq, lk)
+    loss = lambda q_, k_, v_: float((oracle.fwd_padded(q_, k_, v_, scale, causal, lq, lk)[0] * do).sum())
+    h = 1e-6
+    for which, grad, shp in (("q", dq, q.shape), ("k", dk, k.shape), ("v", dv, v.shape)):
+        fd = np.zeros_like(grad)
+        for idx in np.ndindex(shp[2:]):
+            args = {"q": q, "k": k, "v": v}
+            plus = {a: b.copy() for a, b in args.items()}
+            minus = {a: b.copy() for a, b in args.items()}
+            plus[which][(0, 0) + idx] += h
+            minus[which][(0, 0) + idx] -= h
+            fd[(0, 0) + idx] = (loss(plus["q"], plus["k"], plus["v"]) -
+                                loss(minus["q"], minus["k"], minus["v"])) / (2 * h)
+        np.testing.assert_allclose(grad, fd, atol=2e-8, rtol=1e-6, err_msg=which)
+
+
+def test_padded_bad_lengths_are_rejected():
+    q = np.zeros((2, 1, 4, 2))
+    k = np.zeros((2, 1, 3, 2))
+    with pytest.raises(RuntimeError):
+        oracle.fwd_padded(q, k, k, 1.0, False, [4, 5], None)
+    with pytest.raises(RuntimeError):
+        oracle.bwd_padded(q, k, k, q, 1.0, False, None, [-1, 3])

@@ -14,16 +14,19 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 MUTANTS = {
     # forward
     "dropped_scale": ("s[j] = scale * acc;", "s[j] = acc;"),
-    "causal_excludes_diagonal": ("long nvis = causal ? i + 1 : N;", "long nvis = causal ? i : N;"),
-    "causal_sees_one_future_key": ("long nvis = causal ? i + 1 : N; /* keys", "long nvis = causal ? (i + 2 < N ? i + 2 : N) : N; /* keys"),
+    "causal_excludes_diagonal": ("long n = i + Lk - Lq + 1;", "long n = i + Lk - Lq;"),
+    "causal_sees_one_future_key": ("long n = i + Lk - Lq + 1;", "long n = i + Lk - Lq + 2;"),
+    "causal_top_left_aligned": ("long n = i + Lk - Lq + 1;", "long n = i + 1;"),
+    "padding_rows_not_masked": ("if (i >= Lq) return 0; /* padding row */", "/* padding rows not masked */"),
+    "key_lengths_ignored": ("long Lq = lq ? lq[b] : Nq, Lk = lk ? lk[b] : Nk;", "long Lq = lq ? lq[b] : Nq, Lk = Nk;"),
     "no_max_subtraction": ("s[j] = exp(s[j] - m); /* unnormalised weight */", "s[j] = exp(s[j]); /* unnormalised weight */"),
     "lse_without_max": ("*lse = m + log(l);", "*lse = log(l);"),
     "value_transposed": ("o[c] += p * V[j * d + c];", "o[c] += p * V[c * d + j % d];"),
     # backward
     "softmax_grad_sign": ("dSi[j] = Pi[j] * (dSi[j] - D);", "dSi[j] = Pi[j] * (dSi[j] + D);"),
-    "dk_uses_k": ("acc += J->dS[i * N + j] * J->q[i * d + c];", "acc += J->dS[i * N + j] * J->k[i * d + c];"),
+    "dk_uses_k": ("acc += J->dS[i * Nk + j] * J->q[i * d + c];", "acc += J->dS[i * Nk + j] * J->k[i * d + c];"),
     "dq_missing_scale": ("J->dq[i * d + c] = J->scale * acc;", "J->dq[i * d + c] = acc;"),
-    "dv_uses_transposed_p": ("acc += J->P[i * N + j] * J->dout[i * d + c];", "acc += J->P[j * N + i] * J->dout[i * d + c];"),
+    "dv_uses_transposed_p": ("acc += J->P[i * Nk + j] * J->dout[i * d + c];", "acc += J->P[j * Nk + i] * J->dout[i * d + c];"),
 }
 
 PINS = [
@@ -37,6 +40,9 @@ PINS = [
     lambda: pins.test_huge_scores_stay_finite(),
     lambda: pins.test_backward_central_differences(True, 5, 4),
     lambda: pins.test_backward_invariants(True),
+    lambda: pins.test_padded_matches_torch_masked_reference(0, True),
+    lambda: pins.test_padded_matches_torch_masked_reference(1, False),
+    lambda: pins.test_bottom_right_causal_closed_forms(),
 ]
 
 
