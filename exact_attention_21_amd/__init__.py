@@ -7,9 +7,10 @@ the library's kernels.  There is no fallback: if libfa.so is missing or the
 device is not gfx950 the calls raise.
 
 Names mirror the C ABI: fa_fwd, fa_bwd (and its three stages fa_bwd_preprocess,
-fa_bwd_dkdv, fa_bwd_dq), fa_bwd_workspace_size, fa_fwd_plan, fa_bwd_plan,
-fa_status_str.  fwd() and bwd() are conveniences that allocate the
-outputs (and the backward workspace) with torch and call fa_fwd / fa_bwd.
+fa_bwd_dkdv, fa_bwd_dq), fa_fwd_padded, fa_bwd_padded, fa_bwd_workspace_size,
+fa_fwd_plan, fa_bwd_plan, fa_status_str.  fwd(), bwd(), fwd_padded() and
+bwd_padded() are conveniences that allocate the outputs (and the backward
+workspace) with torch and call the corresponding entry point.
 """
 from __future__ import annotations
 
@@ -53,6 +54,11 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_dkdv.restype = I
         L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp, Z, vp]
         L.fa_bwd_dq.restype = I
+        L.fa_fwd_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, I, vp]
+        L.fa_fwd_padded.restype = I
+        L.fa_bwd_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, I,
+                                    vp, Z, vp]
+        L.fa_bwd_padded.restype = I
         L.fa_bwd_workspace_size.argtypes = [I, I, I, I]
         L.fa_bwd_workspace_size.restype = Z
         L.fa_fwd_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(fa_plan_t)]
@@ -222,4 +228,92 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
         workspace = torch.empty(fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, default_scale(d) if scale is None else scale, causal,
            workspace)
+    return dq, dk, dv
+
+
+def _lens_ptr(lens, B, device):
+    """Device int32 [B] length array (or NULL)."""
+    import torch
+    if lens is None:
+        return ctypes.c_void_p(None)
+    if not (isinstance(lens, torch.Tensor) and lens.dtype == torch.int32 and lens.device == device
+            and lens.is_contiguous() and tuple(lens.shape) == (B,)):
+        raise ValueError("sequence lengths must be a contiguous int32 [B] tensor on q's device")
+    return _ptr(lens)
+
+
+def _check_padded(q, k, v):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t in (("k", k), ("v", v)):
+        if t.device != q.device or t.dtype != q.dtype or tuple(t.shape) != (B, H, Nk, d):
+            raise ValueError(f"{name} must be [B, H, Nk, d] with q's device and dtype")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    return B, H, Nq, Nk, d
+
+
+def fa_fwd_padded(q, k, v, o, lse, seqlens_q, seqlens_k, scale: float, causal: bool,
+                  stream=None) -> None:
+    """Forward over padded batches / cross-attention into caller-provided o and lse.
+    seqlens_q, seqlens_k: device int32 [B] valid lengths, or None (all valid)."""
+    import torch
+    B, H, Nq, Nk, d = _check_padded(q, k, v)
+    _check_qkv_like("o", o, q)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be contiguous float32 [B, H, Nq] on q's device")
+    rc = lib().fa_fwd_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_k, B, q.device),
+                             B, H, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q),
+                             _stream(stream))
+    if rc:
+        raise FaError("fa_fwd_padded", rc)
+
+
+def fa_bwd_padded(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, scale: float,
+                  causal: bool, workspace, stream=None) -> None:
+    """Backward of fa_fwd_padded into caller-provided dq, dk, dv."""
+    import torch
+    B, H, Nq, Nk, d = _check_padded(q, k, v)
+    for name, t in (("o", o), ("dout", dout), ("dq", dq)):
+        _check_qkv_like(name, t, q)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_qkv_like(name, t, k)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    rc = lib().fa_bwd_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _lens_ptr(seqlens_q, B, q.device),
+                             _lens_ptr(seqlens_k, B, q.device), B, H, Nq, Nk, d, float(scale),
+                             int(bool(causal)), _dtype_code(q), *_ws(workspace, q), _stream(stream))
+    if rc:
+        raise FaError("fa_bwd_padded", rc)
+
+
+def fwd_padded(q, k, v, seqlens_q=None, seqlens_k=None, causal: bool = False,
+               scale: float | None = None):
+    """Returns (o, lse) for q [B, H, Nq, d], k, v [B, H, Nk, d] and per-batch valid lengths."""
+    import torch
+    B, H, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_padded(q, k, v, o, lse, seqlens_q, seqlens_k, default_scale(d) if scale is None else scale,
+                  causal)
+    return o, lse
+
+
+def bwd_padded(q, k, v, o, dout, lse, seqlens_q=None, seqlens_k=None, causal: bool = False,
+               scale: float | None = None, workspace=None):
+    """Returns (dq, dk, dv) of fwd_padded."""
+    import torch
+    B, H, Nq, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_size(B, H, Nq, d), dtype=torch.uint8, device=q.device)
+    fa_bwd_padded(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k,
+                  default_scale(d) if scale is None else scale, causal, workspace)
     return dq, dk, dv

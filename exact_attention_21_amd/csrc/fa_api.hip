@@ -33,11 +33,24 @@ int check_device() {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+fa::SeqShape seq_shape(int H, int Nq, int Nk, const int *lq, const int *lk) {
+  fa::SeqShape s;
+  s.Nq = Nq;
+  s.Nk = Nk;
+  s.H = H;
+  s.lq = lq;
+  s.lk = lk;
+  return s;
+}
 
 int check_common(int B, int H, int N, int d, int causal, int dtype) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   const long double elems = (long double)B * H * N * (d > 0 ? d : 1);
   if (elems > 4.0e18L) return FA_ERR_SHAPE;
+  // one head is addressed through a 32-bit buffer resource
+  if ((long double)N * (d > 0 ? d : 1) * 2 >= 4294967296.0L) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
@@ -58,10 +71,10 @@ const char *fa_status_str(int s) {
   switch (s) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "null pointer argument";
-    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1; element count too large)";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1; a head or the element count is too large)";
     case FA_ERR_HEAD_DIM: return "head dim must be 64 or 128";
     case FA_ERR_DTYPE: return "dtype must be FA_F16 (0) or FA_BF16 (1)";
-    case FA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FA_ERR_ALIGN: return "tensor pointer not 16-byte aligned, or length array not 4-byte aligned";
     case FA_ERR_WORKSPACE: return "backward workspace too small";
     case FA_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case FA_ERR_LAUNCH: return "kernel launch failed";
@@ -89,15 +102,23 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *pl
   return FA_OK;
 }
 
-int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
-           int N, int d, float scale, int causal, int dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, const int *lq,
+             const int *lk, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+             int dtype, void *stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   fa_plan_t plan;
-  int rc = fa_fwd_plan(B, H, N, d, causal, dtype, &plan);
+  int rc = fa_fwd_plan(B, H, Nq, d, causal, dtype, &plan);
+  if (rc) return rc;
+  rc = check_common(B, H, Nk, d, causal, dtype);
   if (rc) return rc;
   if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
+  if (!aligned4(lq) || !aligned4(lk)) return FA_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
   fa::FwdParams p;
@@ -106,13 +127,29 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
   p.v = v;
   p.o = o;
   p.lse = lse;
-  p.N = N;
-  p.n_qtiles = (N + plan.block_m - 1) / plan.block_m;
+  p.seq = seq_shape(H, Nq, Nk, lq, lk);
+  p.n_qtiles = (Nq + plan.block_m - 1) / plan.block_m;
   p.xcd_grouped = plan.xcd_grouped;
   p.scale_log2 = scale * 1.4426950408889634f;
   const hipError_t e = fa::launch_fwd(p, dtype, d, causal, plan.block_m / 128, plan.grid,
                                       reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+           int N, int d, float scale, int causal, int dtype, void *stream) {
+  return fwd_impl(q, k, v, o, lse, nullptr, nullptr, B, H, N, N, d, scale, causal, dtype, stream);
+}
+
+int fa_fwd_padded(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
+                  int d, float scale, int causal, int dtype, void *stream) {
+  return fwd_impl(q, k, v, o, lse, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale, causal, dtype,
+                  stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
@@ -143,23 +180,28 @@ int fa_bwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *pl
 namespace {
 
 // Shared checks of the backward entry points; fills the parameter block's
-// shape fields and workspace pointers.
-int bwd_setup(int B, int H, int N, int d, float scale, int causal, int dtype, void *workspace,
-              size_t workspace_bytes, fa::BwdParams *p, fa_plan_t *plan) {
-  int rc = fa_bwd_plan(B, H, N, d, causal, dtype, plan);
+// shape fields and workspace pointers.  Q-side tensors have Nq rows, K-side Nk.
+int bwd_setup(int B, int H, int Nq, int Nk, const int *lq, const int *lk, int d, float scale,
+              int causal, int dtype, void *workspace, size_t workspace_bytes, fa::BwdParams *p,
+              fa_plan_t *plan) {
+  int rc = fa_bwd_plan(B, H, Nk, d, causal, dtype, plan);
   if (rc) return rc;
+  rc = check_common(B, H, Nq, d, causal, dtype);
+  if (rc) return rc;
+  if ((long long)(Nq + fa::BWD_DQ_BM - 1) / fa::BWD_DQ_BM * B * H > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
   if (!workspace) return FA_ERR_NULL;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_WORKSPACE;
-  const size_t rows = (size_t)B * H * N;
+  if (!aligned4(lq) || !aligned4(lk)) return FA_ERR_ALIGN;
+  if (workspace_bytes < fa_bwd_workspace_size(B, H, Nq, d)) return FA_ERR_WORKSPACE;
+  const size_t rows = (size_t)B * H * Nq;
   char *ws = static_cast<char *>(workspace);
   std::memset(p, 0, sizeof *p);
   p->dws = reinterpret_cast<float *>(ws);
   p->lse2 = reinterpret_cast<float *>(ws + align256(rows * sizeof(float)));
-  p->N = N;
-  p->n_qtiles = (N + fa::BWD_DQ_BM - 1) / fa::BWD_DQ_BM;
-  p->n_ktiles = (N + fa::BWD_DKDV_BN - 1) / fa::BWD_DKDV_BN;
+  p->seq = seq_shape(H, Nq, Nk, lq, lk);
+  p->n_qtiles = (Nq + fa::BWD_DQ_BM - 1) / fa::BWD_DQ_BM;
+  p->n_ktiles = (Nk + fa::BWD_DKDV_BN - 1) / fa::BWD_DKDV_BN;
   p->xcd_grouped = plan->xcd_grouped;
   p->scale = scale;
   p->scale_log2 = scale * 1.4426950408889634f;
@@ -181,7 +223,8 @@ int fa_bwd_preprocess(const void *o, const void *dout, const float *lse, int B, 
   if (!o || !dout || !lse || !workspace) return FA_ERR_NULL;
   fa::BwdParams p;
   fa_plan_t plan;
-  int rc = bwd_setup(B, H, N, d, 1.f, 0, dtype, workspace, workspace_bytes, &p, &plan);
+  int rc = bwd_setup(B, H, N, N, nullptr, nullptr, d, 1.f, 0, dtype, workspace, workspace_bytes,
+                     &p, &plan);
   if (rc) return rc;
   if (!all_aligned({o, dout, lse})) return FA_ERR_ALIGN;
   rc = check_device();
@@ -200,7 +243,8 @@ int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, v
   if (!q || !k || !v || !dout || !dk || !dv || !workspace) return FA_ERR_NULL;
   fa::BwdParams p;
   fa_plan_t plan;
-  int rc = bwd_setup(B, H, N, d, scale, causal, dtype, workspace, workspace_bytes, &p, &plan);
+  int rc = bwd_setup(B, H, N, N, nullptr, nullptr, d, scale, causal, dtype, workspace,
+                     workspace_bytes, &p, &plan);
   if (rc) return rc;
   if (!all_aligned({q, k, v, dout, dk, dv})) return FA_ERR_ALIGN;
   rc = check_device();
@@ -222,7 +266,8 @@ int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, voi
   if (!q || !k || !v || !dout || !dq || !workspace) return FA_ERR_NULL;
   fa::BwdParams p;
   fa_plan_t plan;
-  int rc = bwd_setup(B, H, N, d, scale, causal, dtype, workspace, workspace_bytes, &p, &plan);
+  int rc = bwd_setup(B, H, N, N, nullptr, nullptr, d, scale, causal, dtype, workspace,
+                     workspace_bytes, &p, &plan);
   if (rc) return rc;
   if (!all_aligned({q, k, v, dout, dq})) return FA_ERR_ALIGN;
   rc = check_device();
@@ -237,14 +282,19 @@ int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, voi
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
-           const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
-           float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
-           void *stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const void *q, const void *k, const void *v, const void *o, const void *dout,
+             const float *lse, void *dq, void *dk, void *dv, const int *lq, const int *lk, int B,
+             int H, int Nq, int Nk, int d, float scale, int causal, int dtype, void *workspace,
+             size_t workspace_bytes, void *stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
   fa::BwdParams p;
   fa_plan_t plan;
-  int rc = bwd_setup(B, H, N, d, scale, causal, dtype, workspace, workspace_bytes, &p, &plan);
+  int rc = bwd_setup(B, H, Nq, Nk, lq, lk, d, scale, causal, dtype, workspace, workspace_bytes,
+                     &p, &plan);
   if (rc) return rc;
   if (!all_aligned({q, k, v, o, dout, lse, dq, dk, dv})) return FA_ERR_ALIGN;
   rc = check_device();
@@ -259,10 +309,30 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
   p.dk = dk;
   p.dv = dv;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = fa::launch_bwd_pre(p, dtype, d, (long)B * H * N, st);
+  hipError_t e = fa::launch_bwd_pre(p, dtype, d, (long)B * H * Nq, st);
   if (e == hipSuccess) e = fa::launch_bwd_dkdv(p, dtype, d, causal, p.n_ktiles * B * H, st);
   if (e == hipSuccess) e = fa::launch_bwd_dq(p, dtype, d, causal, p.n_qtiles * B * H, st);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
+           void *stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, H, N, N, d, scale, causal,
+                  dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_padded(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                  const float *lse, void *dq, void *dk, void *dv, const int *seqlens_q,
+                  const int *seqlens_k, int B, int H, int Nq, int Nk, int d, float scale,
+                  int causal, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale,
+                  causal, dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

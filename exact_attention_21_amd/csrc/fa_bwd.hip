@@ -8,7 +8,7 @@
 //   dS = P (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
 // Three kernels, none with atomics (so every output is bitwise reproducible):
-//   bwd_pre_kernel   D = rowsum(dO * O) and LSE * log2(e), fp32 [B][H][N]
+//   bwd_pre_kernel   D = rowsum(dO * O) and LSE * log2(e), fp32 [B][H][Nq]
 //   bwd_dq_kernel    one workgroup per 128 query rows, K/V tiles streamed through
 //                    LDS (the forward's structure): S^T = K Q^T, dP^T = V dO^T,
 //                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T
@@ -90,7 +90,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
   if (row < rows && sub == 0) {
     dws[row] = acc;
-    lse2[row] = lse[row] * 1.4426950408889634f;
+    const float l = lse[row];  // -inf: the row sees no key; +inf makes its P = 0
+    lse2[row] = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
   }
 }
 
@@ -122,7 +123,6 @@ void bwd_dq_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, keep in an SGPR
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = lane >> 4, s16 = lane & 15;
-  const int N = p.N;
 
   int bh, qt;
   {
@@ -142,26 +142,31 @@ void bwd_dq_kernel(BwdParams p) {
   const int i0 = qt * BM;
   const int wr0 = i0 + 32 * w;
   const int qrow = wr0 + l32;  // this lane's query
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * RB;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + hoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const uint16_t *>(p.dout) + hoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + hoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + hoff, head_bytes);
+  // valid lengths of this batch entry; causal: query i sees keys j <= i + shift
+  const int Nq = p.seq.Nq, Nk = p.seq.Nk;
+  int Lq, Lk;
+  seq_lengths(p.seq, bh / p.seq.H, Lq, Lk);
+  const int shift = Lk - Lq;
+  const size_t qoff = (size_t)bh * (size_t)Nq * D, koff = (size_t)bh * (size_t)Nk * D;
+  // resources end at the valid rows: padding queries and keys read as zeros
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + qoff, (uint32_t)Lq * RB);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const uint16_t *>(p.dout) + qoff, (uint32_t)Lq * RB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + koff, (uint32_t)Lk * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + koff, (uint32_t)Lk * RB);
 
-  const int kend = CAUSAL ? min(N, i0 + BM) : N;
+  const int kend = i0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, i0 + BM + shift)) : Lk;
   const int nt = (kend + BN - 1) / BN;
   const float sl2 = p.scale_log2;
 
-  // per-lane row statistics; rows past N get lse2 = +inf so that P = 0
-  const float lse2 = qrow < N ? p.lse2[(size_t)bh * N + qrow] : __builtin_inff();
-  const float dsum = qrow < N ? p.dws[(size_t)bh * N + qrow] : 0.f;
+  // per-lane row statistics; padding rows get lse2 = +inf so that P = 0
+  const float lse2 = qrow < Lq ? p.lse2[(size_t)bh * Nq + qrow] : __builtin_inff();
+  const float dsum = qrow < Lq ? p.dws[(size_t)bh * Nq + qrow] : 0.f;
 
   // Q and dO fragments: B operands of S^T = K Q^T and dP^T = V dO^T
   u32x4 qf[ND16], dof[ND16];
 #pragma unroll
   for (int db = 0; db < ND16; ++db) {
-    const uint32_t off = (uint32_t)(qrow * D + db * 16 + hi * 8) * 2;  // rows past N read 0
+    const uint32_t off = (uint32_t)(qrow * D + db * 16 + hi * 8) * 2;  // rows past Lq read 0
     qf[db] = bload16(rq, off);
     dof[db] = bload16(rdo, off);
   }
@@ -208,7 +213,7 @@ void bwd_dq_kernel(BwdParams p) {
       t_base[h] = (uint32_t)(row * RB + (((byte >> 4) ^ swz_both<D>(row)) << 4) + (byte & 15));
     }
   }
-  const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+  const int lim = CAUSAL ? min(qrow + shift, Lk - 1) : Lk - 1;  // last visible key
 
   // one step on key tile t held in ring slot SL
   auto step = [&](int t, auto slot) {
@@ -226,7 +231,7 @@ void bwd_dq_kernel(BwdParams p) {
     }
     // P^T = exp2(scale log2e S - LSE log2e), masked; dS^T = P^T (dP^T - D)
     const int j0 = t * BN;
-    const bool need_mask = (CAUSAL && j0 + BN - 1 > wr0) || (j0 + BN > N);
+    const bool need_mask = (CAUSAL && j0 + BN - 1 > wr0 + shift) || (j0 + BN > Lk);
     uint32_t dsk[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -272,18 +277,21 @@ void bwd_dq_kernel(BwdParams p) {
   if (t < nt) step(t, S0{});
   wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
-  // dQ = scale dQ^T^T, rounded to 16 bits
-  if (qrow < N) {
-    uint16_t *dQh = reinterpret_cast<uint16_t *>(p.dq) + hoff;
+  // dQ = scale dQ^T^T, rounded to 16 bits (0 for padding rows)
+  if (qrow < Nq) {
+    uint16_t *dQh = reinterpret_cast<uint16_t *>(p.dq) + qoff;
+    const bool live = qrow < Lq;  // padding rows store zeros
     const float sc = p.scale;
 #pragma unroll
     for (int c = 0; c < ND32; ++c)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int dcol = c * 32 + 8 * rg + 4 * hi;
-        u32x2 st;
-        st[0] = T::pack(dqacc[c][4 * rg] * sc, dqacc[c][4 * rg + 1] * sc);
-        st[1] = T::pack(dqacc[c][4 * rg + 2] * sc, dqacc[c][4 * rg + 3] * sc);
+        u32x2 st = {0u, 0u};
+        if (live) {
+          st[0] = T::pack(dqacc[c][4 * rg] * sc, dqacc[c][4 * rg + 1] * sc);
+          st[1] = T::pack(dqacc[c][4 * rg + 2] * sc, dqacc[c][4 * rg + 3] * sc);
+        }
         *reinterpret_cast<u32x2 *>(dQh + (size_t)qrow * D + dcol) = st;
       }
   }
@@ -327,7 +335,6 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, keep in an SGPR
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = lane >> 4, s16 = lane & 15;
-  const int N = p.N;
 
   int bh, kt;
   {
@@ -346,27 +353,35 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int j0 = kt * BN;
   const int kw0 = j0 + 32 * w;
   const int key = kw0 + l32;  // this lane's key
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * RB;
-  const uint32_t stat_bytes = (uint32_t)N * 4;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + hoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const uint16_t *>(p.dout) + hoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + hoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + hoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse2 + (size_t)bh * N, stat_bytes);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dws + (size_t)bh * N, stat_bytes);
+  // valid lengths of this batch entry; causal: query i sees keys j <= i + shift
+  const int Nq = p.seq.Nq, Nk = p.seq.Nk;
+  int Lq, Lk;
+  seq_lengths(p.seq, bh / p.seq.H, Lq, Lk);
+  const int shift = Lk - Lq;
+  const size_t qoff = (size_t)bh * (size_t)Nq * D, koff = (size_t)bh * (size_t)Nk * D;
+  // resources end at the valid rows: padding rows read Q = dO = 0 and
+  // LSE2 = D = 0 (so they add nothing to dK, dV), padding keys read K = V = 0
+  const uint32_t q_bytes = (uint32_t)Lq * RB, k_bytes = (uint32_t)Lk * RB;
+  const uint32_t stat_bytes = (uint32_t)Lq * 4;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + qoff, q_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const uint16_t *>(p.dout) + qoff, q_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + koff, k_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + koff, k_bytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse2 + (size_t)bh * Nq, stat_bytes);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dws + (size_t)bh * Nq, stat_bytes);
 
   // K and V fragments of this wave's keys: B operands of S = Q K^T, dP = dO V^T
   u32x4 kf[ND16], vf[ND16];
 #pragma unroll
   for (int db = 0; db < ND16; ++db) {
-    const uint32_t off = (uint32_t)(key * D + db * 16 + hi * 8) * 2;  // keys past N read 0
+    const uint32_t off = (uint32_t)(key * D + db * 16 + hi * 8) * 2;  // keys past Lk read 0
     kf[db] = bload16(rk, off);
     vf[db] = bload16(rv, off);
   }
 
-  const int nqt = (N + BM - 1) / BM;
-  const int qt0 = CAUSAL ? j0 / BM : 0;
+  // query tiles with valid rows that see a key of this block (none if all its keys are padding)
+  const int nqt = j0 >= Lk ? 0 : (Lq + BM - 1) / BM;
+  const int qt0 = CAUSAL ? max(0, j0 - shift) / BM : 0;
   const float sl2 = p.scale_log2;
 
   uint32_t dq_off[BPW];
@@ -445,7 +460,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       s = T::mma(lds_read16(qs + fa), kf[db], s);
       dp = T::mma(lds_read16(ds + fa), vf[db], dp);
     }
-    const bool need_mask = CAUSAL && q0 < kw0 + 31;
+    const bool need_mask = CAUSAL && q0 + shift < kw0 + 31;
     uint32_t pk[8], sk[8];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
@@ -456,9 +471,9 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rg + e;
-        // rows past N load LSE2 = D = 0 and Q = dO = 0, so they contribute nothing
+        // rows past Lq load LSE2 = D = 0 and Q = dO = 0, so they contribute nothing
         float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lq[e]));
-        if (need_mask) pr = key <= q0 + qr + e ? pr : 0.f;
+        if (need_mask) pr = key <= q0 + qr + e + shift ? pr : 0.f;
         pv[e] = pr;
         sv[e] = pr * (dp[r] - dq[e]);
       }
@@ -490,7 +505,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2 % NS>;
 
-  const int nsteps = nqt - qt0;
+  const int nsteps = max(0, nqt - qt0);
   issue_step(0, S0{});
   if constexpr (NS == 3) issue_step(1, S1{});
   wait_dma(std::integral_constant<int, NS - 2>{});
@@ -507,21 +522,24 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
-  // dK = scale dK^T^T, dV = dV^T^T, rounded to 16 bits
-  if (key < N) {
-    uint16_t *dKh = reinterpret_cast<uint16_t *>(p.dk) + hoff;
-    uint16_t *dVh = reinterpret_cast<uint16_t *>(p.dv) + hoff;
+  // dK = scale dK^T^T, dV = dV^T^T, rounded to 16 bits (0 for padding keys)
+  if (key < Nk) {
+    uint16_t *dKh = reinterpret_cast<uint16_t *>(p.dk) + koff;
+    uint16_t *dVh = reinterpret_cast<uint16_t *>(p.dv) + koff;
+    const bool live = key < Lk;  // padding keys store zeros (their sums are meaningless)
     const float sc = p.scale;
 #pragma unroll
     for (int c = 0; c < ND32; ++c)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int dcol = c * 32 + 8 * rg + 4 * hi;
-        u32x2 a, b;
-        a[0] = T::pack(dkacc[c][4 * rg] * sc, dkacc[c][4 * rg + 1] * sc);
-        a[1] = T::pack(dkacc[c][4 * rg + 2] * sc, dkacc[c][4 * rg + 3] * sc);
-        b[0] = T::pack(dvacc[c][4 * rg], dvacc[c][4 * rg + 1]);
-        b[1] = T::pack(dvacc[c][4 * rg + 2], dvacc[c][4 * rg + 3]);
+        u32x2 a = {0u, 0u}, b = {0u, 0u};
+        if (live) {
+          a[0] = T::pack(dkacc[c][4 * rg] * sc, dkacc[c][4 * rg + 1] * sc);
+          a[1] = T::pack(dkacc[c][4 * rg + 2] * sc, dkacc[c][4 * rg + 3] * sc);
+          b[0] = T::pack(dvacc[c][4 * rg], dvacc[c][4 * rg + 1]);
+          b[1] = T::pack(dvacc[c][4 * rg + 2], dvacc[c][4 * rg + 3]);
+        }
         *reinterpret_cast<u32x2 *>(dKh + (size_t)key * D + dcol) = a;
         *reinterpret_cast<u32x2 *>(dVh + (size_t)key * D + dcol) = b;
       }

@@ -47,6 +47,7 @@ namespace fa {
 namespace {
 
 constexpr float LAZY_TAU = 8.0f;  // log2 growth of a row max that forces a rescale
+constexpr float M_FLOOR = -1e30f; // initial running max (log2 units)
 constexpr int NSLOT = 2;          // ring slots per K and V (tiles are loaded one step ahead)
 
 // o *= a for an accumulator that lives in AGPRs (rare path): read, scale and
@@ -114,7 +115,6 @@ void fwd_kernel(FwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform, keep in an SGPR
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = lane >> 4, s16 = lane & 15;
-  const int N = p.N;
 
   // ---- which (head, query tile) this workgroup computes
   int bh, qt;
@@ -133,14 +133,20 @@ void fwd_kernel(FwdParams p) {
     qt = CAUSAL ? nq - 1 - r : r;  // causal: longest rows first
   }
   const int i0 = qt * BM;
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * RB;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + hoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + hoff, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + hoff, head_bytes);
+  // valid lengths of this batch entry; causal: query i sees keys j <= i + shift
+  const int Nq = p.seq.Nq, Nk = p.seq.Nk;
+  int Lq, Lk;
+  seq_lengths(p.seq, bh / p.seq.H, Lq, Lk);
+  const int shift = Lk - Lq;
+  const size_t qoff = (size_t)bh * (size_t)Nq * D, koff = (size_t)bh * (size_t)Nk * D;
+  // resources end at the valid rows: padding queries and keys read as zeros
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + qoff, (uint32_t)Lq * RB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + koff, (uint32_t)Lk * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + koff, (uint32_t)Lk * RB);
   const int wr0 = i0 + w * WR;  // first query row of this wave
 
-  const int kend = CAUSAL ? min(N, i0 + BM) : N;
+  // keys the workgroup's rows can see (none if all its rows are padding)
+  const int kend = i0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, i0 + BM + shift)) : Lk;
   const int nt = (kend + BN - 1) / BN;
   const float sl2 = p.scale_log2;
 
@@ -166,7 +172,7 @@ void fwd_kernel(FwdParams p) {
   u32x4 qf[QB][ND16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = wr0 + qb * 32 + l32;  // rows past N read as zeros
+    const int row = wr0 + qb * 32 + l32;  // rows past Lq read as zeros
 #pragma unroll
     for (int db = 0; db < ND16; ++db)
       qf[qb][db] = bload16(rq, (uint32_t)(row * D + db * 16 + hi * 8) * 2);
@@ -180,7 +186,10 @@ void fwd_kernel(FwdParams p) {
   float mrun[QB], lrun[QB];  // running max (log2 units) and this lane's partial row sum
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    mrun[qb] = -__builtin_inff();
+    // a finite floor instead of -inf: a row that sees no key in a tile then
+    // takes exp2(-inf - floor) = 0 rather than exp2(-inf + inf) = NaN, and
+    // the first visible tile always raises the max (alpha = exp2(floor - m) = 0)
+    mrun[qb] = M_FLOOR;
     lrun[qb] = 0.f;
   }
 
@@ -222,14 +231,14 @@ void fwd_kernel(FwdParams p) {
   // masking of tile t: causal diagonal and the ragged key tail
   auto needs_mask = [&](int t) {
     const int j0 = t * BN;
-    return (CAUSAL && j0 + BN - 1 > wr0) || (j0 + BN > N);
+    return (CAUSAL && j0 + BN - 1 > wr0 + shift) || (j0 + BN > Lk);
   };
   auto apply_mask = [&](int t, f32x16 (&s)[QB]) {
     const int j0 = t * BN;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qrow = wr0 + qb * 32 + l32;
-      const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;  // last visible key
+      const int lim = CAUSAL ? min(qrow + shift, Lk - 1) : Lk - 1;  // last visible key
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -335,25 +344,29 @@ void fwd_kernel(FwdParams p) {
   wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
   // ---- epilogue: O = acc / l (rounded to 16 bits), LSE = (m + log2 l) ln 2
-  uint16_t *Oh = reinterpret_cast<uint16_t *>(p.o) + hoff;
-  float *Lh = p.lse + (size_t)bh * N;
+  uint16_t *Oh = reinterpret_cast<uint16_t *>(p.o) + qoff;
+  float *Lh = p.lse + (size_t)bh * Nq;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = lrun[qb] + xhalf(lrun[qb]);
-    const float inv = 1.f / lt;
     const int row = wr0 + qb * 32 + l32;
-    if (row < N) {
+    // padding rows and rows that see no key: O = 0, LSE = -inf
+    const bool live = row < Lq && lt > 0.f;
+    const float inv = 1.f / lt;
+    if (row < Nq) {
 #pragma unroll
       for (int c = 0; c < ND32; ++c)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int dcol = c * 32 + 8 * rg + 4 * hi;
-          u32x2 st;
-          st[0] = T::pack(oacc[qb][c][4 * rg + 0] * inv, oacc[qb][c][4 * rg + 1] * inv);
-          st[1] = T::pack(oacc[qb][c][4 * rg + 2] * inv, oacc[qb][c][4 * rg + 3] * inv);
+          u32x2 st = {0u, 0u};
+          if (live) {
+            st[0] = T::pack(oacc[qb][c][4 * rg + 0] * inv, oacc[qb][c][4 * rg + 1] * inv);
+            st[1] = T::pack(oacc[qb][c][4 * rg + 2] * inv, oacc[qb][c][4 * rg + 3] * inv);
+          }
           *reinterpret_cast<u32x2 *>(Oh + (size_t)row * D + dcol) = st;
         }
-      if (hi == 0) Lh[row] = (mrun[qb] + fast_log2(lt)) * 0.69314718055994531f;
+      if (hi == 0) Lh[row] = live ? (mrun[qb] + fast_log2(lt)) * 0.69314718055994531f : -__builtin_inff();
     }
   }
 }

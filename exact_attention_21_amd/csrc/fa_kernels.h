@@ -30,12 +30,29 @@ constexpr int FWD_BN = 32;
 #define FWD_WAVES_D64 3
 #endif
 
+// Sequence shape of a call.  Query-side tensors (Q, O, dO, dQ, LSE) have Nq
+// rows per head, key-side ones (K, V, dK, dV) Nk.  Batch entry b has
+// Lq = clamp(lq[b], 0, Nq) valid queries and Lk = clamp(lk[b], 0, Nk) valid
+// keys; lq / lk NULL means all valid.  With the causal mask query i sees key j
+// iff j <= i + Lk - Lq (the diagonal ends at the last query and the last key).
+struct SeqShape {
+  int Nq, Nk;
+  int H;
+  const int *lq, *lk;  // device int32 [B] or NULL
+};
+
+// Valid lengths of batch entry b (uniform across the workgroup: scalar loads).
+__device__ __forceinline__ void seq_lengths(const SeqShape &s, int b, int &Lq, int &Lk) {
+  Lq = s.lq ? min(max(s.lq[b], 0), s.Nq) : s.Nq;
+  Lk = s.lk ? min(max(s.lk[b], 0), s.Nk) : s.Nk;
+}
+
 struct FwdParams {
   const void *q, *k, *v;
   void *o;
   float *lse;
-  int N;            // sequence length
-  int n_qtiles;     // ceil(N / BM)
+  SeqShape seq;
+  int n_qtiles;     // ceil(Nq / BM)
   int xcd_grouped;  // 1: B*H is a multiple of 8 and heads are grouped per XCD
   float scale_log2; // scale * log2(e)
 };
@@ -61,11 +78,11 @@ struct BwdParams {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
-  float *dws;       // fp32 [B][H][N] workspace: D = rowsum(dO * O)
-  float *lse2;      // fp32 [B][H][N] workspace: LSE * log2(e)
-  int N;
-  int n_qtiles;     // ceil(N / BWD_DQ_BM)
-  int n_ktiles;     // ceil(N / BWD_DKDV_BN)
+  float *dws;       // fp32 [B][H][Nq] workspace: D = rowsum(dO * O)
+  float *lse2;      // fp32 [B][H][Nq] workspace: LSE * log2(e) (+inf for rows with LSE = -inf)
+  SeqShape seq;
+  int n_qtiles;     // ceil(Nq / BWD_DQ_BM)
+  int n_ktiles;     // ceil(Nk / BWD_DKDV_BN)
   int xcd_grouped;
   float scale;
   float scale_log2;

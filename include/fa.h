@@ -51,7 +51,7 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype_t;
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or the element count overflows */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or a head or the element count is too large */
   FA_ERR_HEAD_DIM = 3,  /* d not in {64, 128} */
   FA_ERR_DTYPE = 4,     /* dtype not FA_F16 / FA_BF16 */
   FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned */
@@ -116,6 +116,42 @@ int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, v
 int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, void *dq,
               int B, int H, int N, int d, float scale, int causal, int dtype,
               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Padded batches and cross-attention.  "Flash Attention application"
+ * (jsqmd.com), section "Notes", recommends the standard causal mask or a
+ * padding mask; llmtrend.com's "Limitations" section notes that cross-attention
+ * (queries and keys from different sequences) needs its own implementation.
+ *
+ * q, o, dout, dq: [B][H][Nq][d]; k, v, dk, dv: [B][H][Nk][d]; lse: [B][H][Nq]
+ * fp32 (all contiguous, 16-byte aligned, in `dtype`).  seqlens_q / seqlens_k
+ * are device int32 arrays [B] (4-byte aligned) giving the valid queries Lq[b]
+ * and valid keys Lk[b] of each batch entry, or NULL for "all valid" (Nq, Nk).
+ * Values are clamped to [0, Nq] and [0, Nk]; they are read on the device, so
+ * they may be produced by earlier work on the same stream.
+ *
+ * For valid query i (< Lq) and valid key j (< Lk) the pair is visible iff
+ * causal == 0 or j <= i + Lk - Lq, i.e. the causal diagonal ends at the last
+ * query and the last key (for Lq == Lk this is the square rule of fa_fwd).
+ * Outputs:
+ *   - valid rows as in fa_fwd over their visible keys;
+ *   - rows with no visible key (Lk == 0, or causal with i < Lq - Lk) and
+ *     padding rows (i >= Lq): O = 0, LSE = -inf;
+ *   - backward: dQ = 0 for those rows, dK = dV = 0 for padding keys (j >= Lk).
+ * Padding entries of the inputs are never read as data.
+ * fa_bwd_padded takes the forward's o and lse and a workspace of
+ * fa_bwd_workspace_size(B, H, Nq, d) bytes; it has fa_bwd's other properties
+ * (no atomics, bitwise reproducible).  Errors as for fa_fwd / fa_bwd, plus
+ * FA_ERR_ALIGN for misaligned length arrays.
+ */
+int fa_fwd_padded(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
+                  int d, float scale, int causal, int dtype, void *stream);
+int fa_bwd_padded(const void *q, const void *k, const void *v, const void *o,
+                  const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                  const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
+                  int d, float scale, int causal, int dtype, void *workspace,
+                  size_t workspace_bytes, void *stream);
 
 /* Launch plan of a forward call (host-only, no GPU needed). */
 typedef struct {
