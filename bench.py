@@ -16,8 +16,9 @@ whole head) on the host's cores.
 
 After the headline step the other configurations of the workload family (the
 sequence-length sweep N = 1k..32k at 32768 tokens per batch, the d=64 variant,
-the non-causal 4096 forward, the 4096 backward) are timed too and reported under
-"sweep" (skip with --no-sweep; --sweep-only runs just those).
+the non-causal 4096 forward, the 4096 backward, a variable-length causal batch
+and a cross-attention shape through the padded entry points) are timed too and
+reported under "sweep" (skip with --no-sweep; --sweep-only runs just those).
 
 Extra modes: --copy-ref MiB runs a plain device copy of known size (the
 reference for scaling hardware byte counters); --fwd-only times the forward alone.
@@ -116,11 +117,25 @@ def cpu_baseline(bits, w, max_bwd_n):
             "sample": sample + f"; nominal FLOP {flop:.3e} in {secs:.1f} s"}
 
 
+def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
+    """(query, key) pairs of one head with valid lengths Lq, Lk (causal aligned to the
+    last query and key): the work unit of the padded FLOP count."""
+    if not causal:
+        return Lq * Lk
+    # row i sees min(Lk, max(0, i + Lk - Lq + 1)) keys
+    total = 0
+    for i in range(Lq):
+        total += min(Lk, max(0, i + Lk - Lq + 1))
+    return total
+
+
 def sweep(fa, device, steps, warmup):
     """Forward and backward timings over the other configurations of the workload
     family (sequence-length sweep at 32768 tokens per batch, the d=64 variant, the
-    non-causal 4096 forward and the 4096 backward).  Inputs are seeded N(0,1)
-    draws made on the device (timing only; parity is the tests' job)."""
+    non-causal 4096 forward, the 4096 backward, a variable-length causal batch and a
+    cross-attention shape).  Inputs are seeded N(0,1) draws made on the device
+    (timing only; parity is the tests' job).  Padded workloads count FLOP over the
+    visible pairs only: 4 d per pair forward, 2.5x that backward."""
     import torch
     import fa_inputs
     stream = torch.cuda.current_stream()
@@ -129,13 +144,21 @@ def sweep(fa, device, steps, warmup):
         if name.startswith("c1_") or name.startswith("c3_"):
             continue  # c1 is the oracle-sized case; c3 is the headline above
         B, H, N, d, causal = c["B"], c["H"], c["N"], c["d"], c["causal"]
+        Nk = c.get("Nk", N)
+        padded = "len_lo" in c or Nk != N
         tdt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float16
         gen = torch.Generator(device=device).manual_seed(c["seed"])
-        q, k, v, do = (torch.randn((B, H, N, d), generator=gen, device=device, dtype=torch.float32).to(tdt)
-                       for _ in range(4))
+        draw = lambda n: torch.randn((B, H, n, d), generator=gen, device=device,
+                                     dtype=torch.float32).to(tdt)
+        q, do = draw(N), draw(N)
+        k, v = draw(Nk), draw(Nk)
+        lens = None
+        if "len_lo" in c:
+            lens = fa_inputs.seq_lengths(B, c["len_lo"], c["len_hi"], c["seed"])
+        lq = lk = None if lens is None else torch.from_numpy(lens).to(device)
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=device)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
         ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=device)
         scale = 1 / math.sqrt(d)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -143,17 +166,31 @@ def sweep(fa, device, steps, warmup):
             e = ev[i - warmup] if i >= warmup else None
             if e:
                 e[0].record(stream)
-            fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
+            if padded:
+                fa.fa_fwd_padded(q, k, v, o, lse, lq, lk, scale, causal, stream)
+            else:
+                fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
             if e:
                 e[1].record(stream)
-            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, ws, stream)
+            if padded:
+                fa.fa_bwd_padded(q, k, v, o, do, lse, dq, dk, dv, lq, lk, scale, causal, ws, stream)
+            else:
+                fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, ws, stream)
             if e:
                 e[2].record(stream)
         torch.cuda.synchronize()
-        f_fwd, f_bwd = nominal_flop(B, H, N, d, causal)
+        if padded:
+            pairs = sum(visible_pairs(int(lens[b]) if lens is not None else N,
+                                      int(lens[b]) if lens is not None else Nk, causal)
+                        for b in range(B)) * H
+            f_fwd = 4.0 * d * pairs
+            f_bwd = 2.5 * f_fwd
+        else:
+            f_fwd, f_bwd = nominal_flop(B, H, N, d, causal)
         fms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
         bms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-        res[name] = {"B": B, "H": H, "N": N, "d": d, "dtype": c["dtype"], "causal": causal,
+        res[name] = {"B": B, "H": H, "N": N, "Nk": Nk, "d": d, "dtype": c["dtype"], "causal": causal,
+                     "lengths": None if lens is None else [int(x) for x in lens],
                      "fwd_ms": fms, "fwd_tflops": f_fwd / (fms * 1e-3) / 1e12,
                      "bwd_ms": bms, "bwd_tflops": f_bwd / (bms * 1e-3) / 1e12}
         log(f"[bench] sweep {name}: fwd {fms:.3f} ms ({res[name]['fwd_tflops']:.0f} TFLOP/s)  "

@@ -69,7 +69,15 @@ def qkv_bits(B: int, H: int, N: int, d: int, dtype: str, seed: int, with_dout: b
     return tuple(normal_bits(n, dtype, seed, s).reshape(B, H, N, d) for s in streams)
 
 
+def seq_lengths(B: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """B valid sequence lengths drawn uniformly from [lo, hi] (int32), for padded batches."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    return rng.integers(lo, hi + 1, size=B).astype(np.int32)
+
+
 # The workloads: shapes, dtypes, mask mode and seeds (no arithmetic).
+# Padded / cross-attention workloads add Nk (keys per head; default N) and
+# len_lo / len_hi (per-batch valid lengths, the same for queries and keys).
 CONFIGS = {
     "c1_fwd_n256_d64_f16": dict(B=1, H=2, N=256, d=64, dtype="f16", causal=False, seed=BASE_SEED + 1, bwd=False),
     "c2_fwd_n4096_d128_bf16": dict(B=1, H=32, N=4096, d=128, dtype="bf16", causal=False, seed=BASE_SEED + 2, bwd=False),
@@ -81,4 +89,8 @@ CONFIGS = {
     "c4_causal_n16384_d64_f16": dict(B=2, H=32, N=16384, d=64, dtype="f16", causal=True, seed=BASE_SEED + 45, bwd=False),
     "c5_bwd_causal_n4096_d128_bf16": dict(B=2, H=16, N=4096, d=128, dtype="bf16", causal=True, seed=BASE_SEED + 5, bwd=True),
     "c3_bwd_causal_n8192_d128_bf16": dict(B=4, H=32, N=8192, d=128, dtype="bf16", causal=True, seed=BASE_SEED + 6, bwd=True),
+    "p1_varlen_causal_b8_n4096_d128_bf16": dict(B=8, H=16, N=4096, d=128, dtype="bf16", causal=True,
+                                                seed=BASE_SEED + 61, bwd=True, len_lo=512, len_hi=4096),
+    "p2_cross_q4096_k16384_d128_bf16": dict(B=2, H=16, N=4096, Nk=16384, d=128, dtype="bf16",
+                                            causal=False, seed=BASE_SEED + 62, bwd=True),
 }
