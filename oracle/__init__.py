@@ -10,10 +10,13 @@ Functions:
   fwd_rows(q, k, v, scale, causal, rows) -> (o, lse)   selected flat rows b*H*N+h*N+i
   bwd(q, k, v, dout, scale, causal)      -> (dq, dk, dv)
   bwd_heads(q, k, v, dout, scale, causal, heads) -> (dq, dk, dv) for heads b*H+h
-  fwd_padded(q, k, v, scale, causal, lq, lk)        -> (o, lse)
-  bwd_padded(q, k, v, dout, scale, causal, lq, lk)  -> (dq, dk, dv)
+  fwd_padded(q, k, v, scale, causal, lq, lk, dropout)        -> (o, lse)
+  bwd_padded(q, k, v, dout, scale, causal, lq, lk, dropout)  -> (dq, dk, dv)
       q, dout [B, H, Nq, d]; k, v [B, H, Nk, d]; lq, lk per-batch valid lengths
-      (None = all valid); causal is aligned to the last query and key.
+      (None = all valid); causal is aligned to the last query and key;
+      dropout = (p8, seed, offset) or None (drop probability p8 / 256, 64-bit
+      seed, 32-bit offset; see oracle.c).
+  philox4x32_10(counter[4], key[2]) -> 4 words;  dropout_mask(B, H, Nq, Nk, p8, seed, offset)
 Inputs are float64 arrays [B, H, N, d] (exactly widened 16-bit values).
 """
 from __future__ import annotations
@@ -56,10 +59,19 @@ def _load():
         lib.oracle_bwd_heads.restype = I
         lib.oracle_bwd.argtypes = [dp, dp, dp, dp, L, L, L, L, D, I, dp, dp, dp, I]
         lib.oracle_bwd.restype = I
-        lib.oracle_fwd_padded.argtypes = [dp, dp, dp, L, L, L, L, L, lp, lp, D, I, dp, dp]
+        U = ctypes.c_uint32
+        up = ctypes.POINTER(ctypes.c_uint32)
+        lib.oracle_fwd_padded.argtypes = [dp, dp, dp, L, L, L, L, L, lp, lp, D, I, ctypes.c_uint, U, U, U,
+                                          dp, dp]
         lib.oracle_fwd_padded.restype = I
-        lib.oracle_bwd_padded.argtypes = [dp, dp, dp, dp, L, L, L, L, L, lp, lp, D, I, dp, dp, dp, I]
+        lib.oracle_bwd_padded.argtypes = [dp, dp, dp, dp, L, L, L, L, L, lp, lp, D, I, ctypes.c_uint, U, U,
+                                          U, dp, dp, dp, I]
         lib.oracle_bwd_padded.restype = I
+        lib.oracle_philox4x32_10.argtypes = [up, up, up]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_dropout_mask.argtypes = [L, L, L, ctypes.c_uint, U, U, U,
+                                            ctypes.POINTER(ctypes.c_ubyte)]
+        lib.oracle_dropout_mask.restype = I
         _lib = lib
     return _lib
 
@@ -145,7 +157,37 @@ def _lens(x, B):
     return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_long))
 
 
-def fwd_padded(q, k, v, scale: float, causal: bool, lq=None, lk=None):
+def _dropout(dropout):
+    """(p8, seed_lo, seed_hi, offset) from (p8, seed, offset) or None."""
+    if dropout is None:
+        return 0, 0, 0, 0
+    p8, seed, offset = dropout
+    if not 0 <= int(p8) <= 255:
+        raise ValueError("p8 must be in [0, 255]")
+    seed = int(seed) & ((1 << 64) - 1)
+    return int(p8), seed & 0xFFFFFFFF, seed >> 32, int(offset) & 0xFFFFFFFF
+
+
+def philox4x32_10(counter, key):
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in counter])
+    k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (ctypes.c_uint32 * 4)()
+    _load().oracle_philox4x32_10(c, k, out)
+    return [int(x) for x in out]
+
+
+def dropout_mask(B, H, Nq, Nk, p8, seed, offset):
+    """bool [B, H, Nq, Nk]: pairs kept by dropout (see oracle.c)."""
+    p8, slo, shi, off = _dropout((p8, seed, offset))
+    keep = np.zeros((B, H, Nq, Nk), np.uint8)
+    rc = _load().oracle_dropout_mask(B * H, Nq, Nk, p8, slo, shi, off,
+                                     keep.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)))
+    if rc:
+        raise RuntimeError(f"oracle_dropout_mask failed ({rc})")
+    return keep.astype(bool)
+
+
+def fwd_padded(q, k, v, scale: float, causal: bool, lq=None, lk=None, dropout=None):
     q, k, v = _as4(q), _as4(k), _as4(v)
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
@@ -156,13 +198,14 @@ def fwd_padded(q, k, v, scale: float, causal: bool, lq=None, lk=None):
     o = np.empty_like(q)
     lse = np.empty((B, H, Nq), np.float64)
     rc = _load().oracle_fwd_padded(_p(q), _p(k), _p(v), B, H, Nq, Nk, d, lqp, lkp, float(scale),
-                                   int(bool(causal)), _p(o), _p(lse))
+                                   int(bool(causal)), *_dropout(dropout), _p(o), _p(lse))
     if rc:
         raise RuntimeError(f"oracle_fwd_padded failed ({rc})")
     return o, lse
 
 
-def bwd_padded(q, k, v, dout, scale: float, causal: bool, lq=None, lk=None, threads: int | None = None):
+def bwd_padded(q, k, v, dout, scale: float, causal: bool, lq=None, lk=None, dropout=None,
+               threads: int | None = None):
     q, k, v, dout = _as4(q), _as4(k), _as4(v), _as4(dout)
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
@@ -174,8 +217,8 @@ def bwd_padded(q, k, v, dout, scale: float, causal: bool, lq=None, lk=None, thre
     dk = np.empty_like(k)
     dv = np.empty_like(k)
     rc = _load().oracle_bwd_padded(_p(q), _p(k), _p(v), _p(dout), B, H, Nq, Nk, d, lqp, lkp,
-                                   float(scale), int(bool(causal)), _p(dq), _p(dk), _p(dv),
-                                   threads or default_threads())
+                                   float(scale), int(bool(causal)), *_dropout(dropout), _p(dq),
+                                   _p(dk), _p(dv), threads or default_threads())
     if rc:
         raise RuntimeError(f"oracle_bwd_padded failed ({rc})")
     return dq, dk, dv

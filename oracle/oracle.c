@@ -46,9 +46,27 @@
  * diagonal is aligned to the last query and the last key, which for Lq = Lk is
  * the square rule above.  A row with no visible key and every padding row has
  * O = 0 and LSE = -inf and contributes nothing to the gradients.
+ *
+ * Dropout on the attention weights ("MHA tuning, part 1", section "notes in
+ * practice": the dropout mask has to be generated block by block during the
+ * fused computation, so the backward regenerates the same mask).  With drop
+ * threshold p8 in [0, 255] (drop probability p8 / 256), pair (i, j) of head
+ * bh = b*H + h is kept iff byte (j mod 4) of word (i mod 4) of
+ *   Philox4x32-10(counter = (j / 4, i / 4, bh, offset), key = (seed_lo, seed_hi))
+ * is >= p8, and kept weights are scaled by 256 / (256 - p8):
+ *   O_i = sum_j P_ij Z_ij V_j,  Z_ij = keep_ij * 256 / (256 - p8).
+ * P (and so LSE) is the softmax before dropout.  Gradients:
+ *   dV_j = sum_i P_ij Z_ij dO_i, dP_ij = Z_ij (dO_i . V_j), D_i = sum_j P_ij dP_ij,
+ *   dS_ij = P_ij (dP_ij - D_i), dQ, dK as above.
+ * Philox4x32-10 is the counter-based generator of Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3" (SC'11): ten rounds of two
+ * 32x32->64-bit multiplications by 0xD2511F53 and 0xCD9E8D57 whose halves are
+ * permuted and xored with the key, the key advanced by (0x9E3779B9, 0xBB67AE85)
+ * between rounds.
  */
 #include <math.h>
 #include <pthread.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -70,7 +88,8 @@ static long visible_keys(long i, long Lq, long Lk, int causal) {
  * P = softmax(s), o = P V, lse = m + log(sum exp(s - m)); a row with no
  * visible key gets o = 0, lse = -inf.  `s` is scratch of length nvis. */
 static void fwd_row(const double *q, const double *K, const double *V, long nvis,
-                    long d, double scale, double *o, double *lse, double *s) {
+                    long d, double scale, const double *z, double *o, double *lse,
+                    double *s) {
   if (nvis == 0) {
     for (long c = 0; c < d; ++c) o[c] = 0.0;
     *lse = -INFINITY;
@@ -91,6 +110,7 @@ static void fwd_row(const double *q, const double *K, const double *V, long nvis
   for (long c = 0; c < d; ++c) o[c] = 0.0;
   for (long j = 0; j < nvis; ++j) {
     double p = s[j] / l;
+    if (z) p *= z[j]; /* dropout multiplier (0 or 256 / (256 - p8)) */
     for (long c = 0; c < d; ++c) o[c] += p * V[j * d + c];
   }
   *lse = m + log(l);
@@ -117,7 +137,7 @@ static void *fwd_worker(void *arg) {
     const double *Kh = J->k + bh * J->N * J->d;
     const double *Vh = J->v + bh * J->N * J->d;
     fwd_row(J->q + flat * J->d, Kh, Vh, visible_keys(i, J->N, J->N, J->causal), J->d,
-            J->scale, J->o + r * J->d, J->lse + r, s);
+            J->scale, NULL, J->o + r * J->d, J->lse + r, s);
   }
   free(s);
   return NULL;
@@ -178,6 +198,56 @@ int oracle_fwd(const double *q, const double *k, const double *v, long B,
 }
 
 /* ------------------------------------------------------------------------ */
+/* dropout mask: Philox4x32-10 (see the header)                               */
+/* ------------------------------------------------------------------------ */
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t x[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+  uint32_t k[2] = {key[0], key[1]};
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) { /* key schedule: a Weyl sequence */
+      k[0] += 0x9E3779B9u;
+      k[1] += 0xBB67AE85u;
+    }
+    uint64_t a = (uint64_t)0xD2511F53u * x[0];
+    uint64_t b = (uint64_t)0xCD9E8D57u * x[2];
+    uint32_t y0 = (uint32_t)(b >> 32) ^ x[1] ^ k[0];
+    uint32_t y1 = (uint32_t)b;
+    uint32_t y2 = (uint32_t)(a >> 32) ^ x[3] ^ k[1];
+    uint32_t y3 = (uint32_t)a;
+    x[0] = y0; x[1] = y1; x[2] = y2; x[3] = y3;
+  }
+  memcpy(out, x, sizeof x);
+}
+
+typedef struct {
+  unsigned p8;       /* drop threshold 0..255; 0 = no dropout */
+  uint32_t seed_lo, seed_hi, offset;
+} dropout_spec;
+
+/* Z_ij of pair (i, j) of head bh: 0 (dropped) or 256 / (256 - p8). */
+static double dropout_mult(const dropout_spec *dr, long bh, long i, long j) {
+  uint32_t ctr[4] = {(uint32_t)(j >> 2), (uint32_t)(i >> 2), (uint32_t)bh, dr->offset};
+  uint32_t key[2] = {dr->seed_lo, dr->seed_hi};
+  uint32_t r[4];
+  oracle_philox4x32_10(ctr, key, r);
+  unsigned byte = (r[i & 3] >> (8 * (j & 3))) & 0xFFu;
+  return byte >= dr->p8 ? 256.0 / (256.0 - (double)dr->p8) : 0.0;
+}
+
+/* keep[bh][i][j] (0/1 bytes) for every pair of B*H heads of Nq x Nk. */
+int oracle_dropout_mask(long BH, long Nq, long Nk, unsigned p8, uint32_t seed_lo,
+                        uint32_t seed_hi, uint32_t offset, unsigned char *keep) {
+  if (!keep || BH < 1 || Nq < 1 || Nk < 1 || p8 > 255) return 1;
+  dropout_spec dr = {p8, seed_lo, seed_hi, offset};
+  for (long bh = 0; bh < BH; ++bh)
+    for (long i = 0; i < Nq; ++i)
+      for (long j = 0; j < Nk; ++j)
+        keep[(bh * Nq + i) * Nk + j] = dropout_mult(&dr, bh, i, j) != 0.0;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* backward, one head at a time, with the N x N matrices P and dS formed      */
 /* ------------------------------------------------------------------------ */
 
@@ -185,6 +255,9 @@ typedef struct {
   const double *q, *dout;         /* this head, [Nq][d] */
   const double *k, *v;            /* this head, [Nk][d] */
   double *P, *dS;                 /* [Nq][Nk] */
+  double *Z;                      /* [Nq][Nk] dropout multipliers, or NULL */
+  const dropout_spec *drop;       /* used when Z != NULL */
+  long bh;                        /* head index b*H + h (dropout counter) */
   double *dq;                     /* this head, [Nq][d] */
   double *dk, *dv;                /* this head, [Nk][d] */
   long Nq, Nk, Lq, Lk, d;         /* Lq, Lk: valid queries / keys of this batch entry */
@@ -216,13 +289,19 @@ static void *bwd_worker(void *arg) {
       }
       for (long j = 0; j < nvis; ++j) Pi[j] /= l;
       for (long j = nvis; j < Nk; ++j) Pi[j] = 0.0; /* masked: weight 0 */
+      if (J->Z)
+        for (long j = 0; j < Nk; ++j) J->Z[i * Nk + j] = dropout_mult(J->drop, J->bh, i, j);
     }
   } else if (J->phase == 1) {
-    /* dV_j = sum_i P_ij dO_i */
+    /* dV_j = sum_i P_ij Z_ij dO_i */
     for (long j = J->a0; j < J->a1; ++j)
       for (long c = 0; c < d; ++c) {
         double acc = 0.0;
-        for (long i = 0; i < Nq; ++i) acc += J->P[i * Nk + j] * J->dout[i * d + c];
+        for (long i = 0; i < Nq; ++i) {
+          double w = J->P[i * Nk + j];
+          if (J->Z) w *= J->Z[i * Nk + j];
+          acc += w * J->dout[i * d + c];
+        }
         J->dv[j * d + c] = acc;
       }
   } else if (J->phase == 2) {
@@ -234,6 +313,7 @@ static void *bwd_worker(void *arg) {
       for (long j = 0; j < Nk; ++j) {
         double acc = 0.0;
         for (long c = 0; c < d; ++c) acc += J->dout[i * d + c] * J->v[j * d + c];
+        if (J->Z) acc *= J->Z[i * Nk + j];
         dSi[j] = acc; /* dP for now */
       }
       double D = 0.0;
@@ -344,24 +424,35 @@ static int lengths_ok(const long *lq, const long *lk, long B, long Nq, long Nk) 
 /* Forward over every row: o [B][H][Nq][d], lse [B][H][Nq]. */
 int oracle_fwd_padded(const double *q, const double *k, const double *v, long B,
                       long H, long Nq, long Nk, long d, const long *lq,
-                      const long *lk, double scale, int causal, double *o,
+                      const long *lk, double scale, int causal, unsigned p8,
+                      uint32_t seed_lo, uint32_t seed_hi, uint32_t offset, double *o,
                       double *lse) {
   if (!q || !k || !v || !o || !lse) return 1;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return 2;
-  if (!lengths_ok(lq, lk, B, Nq, Nk)) return 3;
+  if (!lengths_ok(lq, lk, B, Nq, Nk) || p8 > 255) return 3;
+  dropout_spec dr = {p8, seed_lo, seed_hi, offset};
   double *s = (double *)malloc(sizeof(double) * (size_t)Nk);
-  if (!s) return 5;
+  double *z = p8 ? (double *)malloc(sizeof(double) * (size_t)Nk) : NULL;
+  if (!s || (p8 && !z)) {
+    free(s);
+    free(z);
+    return 5;
+  }
   for (long b = 0; b < B; ++b) {
     long Lq = lq ? lq[b] : Nq, Lk = lk ? lk[b] : Nk;
     for (long h = 0; h < H; ++h) {
       long bh = b * H + h;
-      for (long i = 0; i < Nq; ++i)
+      for (long i = 0; i < Nq; ++i) {
+        if (z)
+          for (long j = 0; j < Nk; ++j) z[j] = dropout_mult(&dr, bh, i, j);
         fwd_row(q + (bh * Nq + i) * d, k + bh * Nk * d, v + bh * Nk * d,
-                visible_keys(i, Lq, Lk, causal), d, scale, o + (bh * Nq + i) * d,
+                visible_keys(i, Lq, Lk, causal), d, scale, z, o + (bh * Nq + i) * d,
                 lse + bh * Nq + i, s);
+      }
     }
   }
   free(s);
+  free(z);
   return 0;
 }
 
@@ -369,18 +460,22 @@ int oracle_fwd_padded(const double *q, const double *k, const double *v, long B,
 int oracle_bwd_padded(const double *q, const double *k, const double *v,
                       const double *dout, long B, long H, long Nq, long Nk, long d,
                       const long *lq, const long *lk, double scale, int causal,
+                      unsigned p8, uint32_t seed_lo, uint32_t seed_hi, uint32_t offset,
                       double *dq, double *dk, double *dv, int nthreads) {
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return 2;
-  if (!lengths_ok(lq, lk, B, Nq, Nk)) return 3;
+  if (!lengths_ok(lq, lk, B, Nq, Nk) || p8 > 255) return 3;
+  dropout_spec dr = {p8, seed_lo, seed_hi, offset};
   int T = clamp_threads(nthreads);
   if (T > Nq) T = (int)Nq;
   if (T > Nk) T = (int)Nk;
   double *P = (double *)malloc(sizeof(double) * (size_t)Nq * (size_t)Nk);
   double *dS = (double *)malloc(sizeof(double) * (size_t)Nq * (size_t)Nk);
-  if (!P || !dS) {
+  double *Z = p8 ? (double *)malloc(sizeof(double) * (size_t)Nq * (size_t)Nk) : NULL;
+  if (!P || !dS || (p8 && !Z)) {
     free(P);
     free(dS);
+    free(Z);
     return 5;
   }
   int err = 0;
@@ -394,9 +489,11 @@ int oracle_bwd_padded(const double *q, const double *k, const double *v,
     base.dq = dq + bh * Nq * d; base.dk = dk + bh * Nk * d; base.dv = dv + bh * Nk * d;
     base.Nq = Nq; base.Nk = Nk; base.Lq = lq ? lq[b] : Nq; base.Lk = lk ? lk[b] : Nk;
     base.d = d; base.scale = scale; base.causal = causal;
+    base.Z = Z; base.drop = &dr; base.bh = bh;
     for (int phase = 0; phase < 4 && !err; ++phase) err = run_phase(&base, phase, T);
   }
   free(P);
   free(dS);
+  free(Z);
   return err;
 }

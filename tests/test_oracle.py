@@ -465,3 +465,119 @@ def test_padded_bad_lengths_are_rejected():
         oracle.fwd_padded(q, k, k, 1.0, False, [4, 5], None)
     with pytest.raises(RuntimeError):
         oracle.bwd_padded(q, k, k, q, 1.0, False, None, [-1, 3])
+
+
+# --------------------------------------------------------------------------
+# dropout: Philox4x32-10 (published known answers), the mask rule, keep rate,
+# unbiasedness, a masked torch fp64 reference and finite differences
+# --------------------------------------------------------------------------
+
+def test_philox_known_answers():
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
+        kat = json.load(f)
+    for vec in kat["vectors"]:
+        out = oracle.philox4x32_10([int(x, 16) for x in vec["counter"]], [int(x, 16) for x in vec["key"]])
+        assert out == [int(x, 16) for x in vec["out"]]
+
+
+def test_dropout_mask_follows_the_documented_rule():
+    # pair (i, j) of head bh kept iff byte j%4 of word i%4 of
+    # Philox(counter = (j/4, i/4, bh, offset), key = (seed lo, seed hi)) >= p8
+    B, H, Nq, Nk, p8, seed, offset = 2, 3, 9, 13, 77, 0x0123456789ABCDEF, 5
+    keep = oracle.dropout_mask(B, H, Nq, Nk, p8, seed, offset)
+    rng = np.random.default_rng(7)
+    for _ in range(60):
+        b, h, i, j = (int(rng.integers(0, n)) for n in (B, H, Nq, Nk))
+        out = oracle.philox4x32_10([j // 4, i // 4, b * H + h, offset], [seed & 0xFFFFFFFF, seed >> 32])
+        byte = (out[i % 4] >> (8 * (j % 4))) & 0xFF
+        assert keep[b, h, i, j] == (byte >= p8)
+
+
+@pytest.mark.parametrize("p8", [0, 26, 128, 255])
+def test_dropout_keep_rate(p8):
+    keep = oracle.dropout_mask(2, 4, 64, 96, p8, 42, 0)
+    n, p = keep.size, 1 - p8 / 256
+    sigma = math.sqrt(n * p * (1 - p))
+    assert abs(keep.sum() - n * p) <= 5 * sigma + (0 if 0 < p < 1 else 0.5)
+    # different offsets and seeds give different masks
+    if 0 < p8 < 255:
+        assert not np.array_equal(keep, oracle.dropout_mask(2, 4, 64, 96, p8, 42, 1))
+        assert not np.array_equal(keep, oracle.dropout_mask(2, 4, 64, 96, p8, 43, 0))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_zero_equals_no_dropout(causal):
+    q, k, v, do = (rnd((2, 2, 21, 8), 300 + i) for i in range(4))
+    a = oracle.fwd_padded(q, k, v, 0.3, causal)
+    b = oracle.fwd_padded(q, k, v, 0.3, causal, dropout=(0, 99, 3))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    ga = oracle.bwd_padded(q, k, v, do, 0.3, causal)
+    gb = oracle.bwd_padded(q, k, v, do, 0.3, causal, dropout=(0, 99, 3))
+    for x, y in zip(ga, gb):
+        assert np.array_equal(x, y)
+
+
+def torch_dropout_reference(q, k, v, dout, scale, causal, keep, p8):
+    """torch fp64: O = (softmax(S) * Z) V with Z = keep * 256 / (256 - p8); autograd."""
+    import torch
+    Nq, Nk = q.shape[2], k.shape[2]
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    Q, K, V = t(q), t(k), t(v)
+    s = torch.matmul(Q, K.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        mask = torch.from_numpy(~visible_mask(Nq, Nk, Nq, Nk, True))
+        s = s.masked_fill(mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    z = torch.from_numpy(keep.astype(np.float64)) * (256.0 / (256.0 - p8))
+    o = torch.matmul(torch.softmax(s, dim=-1) * z, V)
+    o.backward(torch.tensor(dout, dtype=torch.float64))
+    return o.detach().numpy(), lse.detach().numpy(), Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_matches_torch_masked_reference(causal):
+    B, H, Nq, Nk, d, p8, seed, offset = 2, 2, 27, 35 if not causal else 27, 8, 51, 1234, 9
+    q, do = rnd((B, H, Nq, d), 310), rnd((B, H, Nq, d), 311)
+    k, v = rnd((B, H, Nk, d), 312), rnd((B, H, Nk, d), 313)
+    drop = (p8, seed, offset)
+    o, lse = oracle.fwd_padded(q, k, v, 0.45, causal, dropout=drop)
+    dq, dk, dv = oracle.bwd_padded(q, k, v, do, 0.45, causal, dropout=drop)
+    keep = oracle.dropout_mask(B, H, Nq, Nk, *drop)
+    to, tl, tdq, tdk, tdv = torch_dropout_reference(q, k, v, do, 0.45, causal, keep, p8)
+    for got, ref in ((o, to), (lse, tl), (dq, tdq), (dk, tdk), (dv, tdv)):
+        np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def test_dropout_is_unbiased():
+    # E[O] over dropout masks is the output without dropout: average over offsets
+    q, k, v = rnd((1, 1, 6, 4), 320), rnd((1, 1, 6, 4), 321), rnd((1, 1, 6, 4), 322)
+    ref, _ = oracle.fwd_padded(q, k, v, 0.5, False)
+    n = 3000
+    acc = np.zeros_like(ref)
+    for off in range(n):
+        acc += oracle.fwd_padded(q, k, v, 0.5, False, dropout=(96, 2024, off))[0]
+    # per-element std of one sample is below max|V|; 5 standard errors
+    tol = 5 * np.abs(v).max() * math.sqrt((96 / 256) / (1 - 96 / 256)) / math.sqrt(n)
+    np.testing.assert_allclose(acc / n, ref, atol=tol)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_backward_central_differences(causal):
+    Nq = Nk = 5
+    d = 3
+    q, k, v, do = (rnd((1, 1, Nq, d), 330 + i) for i in range(4))
+    drop = (100, 77, 1)
+    dq, dk, dv = oracle.bwd_padded(q, k, v, do, 0.6, causal, dropout=drop)
+    loss = lambda q_, k_, v_: float((oracle.fwd_padded(q_, k_, v_, 0.6, causal, dropout=drop)[0] * do).sum())
+    h = 1e-6
+    for which, grad in (("q", dq), ("k", dk), ("v", dv)):
+        fd = np.zeros_like(grad)
+        for idx in np.ndindex(grad.shape[2:]):
+            args = {"q": q, "k": k, "v": v}
+            plus = {a: b.copy() for a, b in args.items()}
+            minus = {a: b.copy() for a, b in args.items()}
+            plus[which][(0, 0) + idx] += h
+            minus[which][(0, 0) + idx] -= h
+            fd[(0, 0) + idx] = (loss(plus["q"], plus["k"], plus["v"]) -
+                                loss(minus["q"], minus["k"], minus["v"])) / (2 * h)
+        np.testing.assert_allclose(grad, fd, atol=2e-8, rtol=1e-6, err_msg=which)

@@ -26,7 +26,13 @@ MUTANTS = {
     "softmax_grad_sign": ("dSi[j] = Pi[j] * (dSi[j] - D);", "dSi[j] = Pi[j] * (dSi[j] + D);"),
     "dk_uses_k": ("acc += J->dS[i * Nk + j] * J->q[i * d + c];", "acc += J->dS[i * Nk + j] * J->k[i * d + c];"),
     "dq_missing_scale": ("J->dq[i * d + c] = J->scale * acc;", "J->dq[i * d + c] = acc;"),
-    "dv_uses_transposed_p": ("acc += J->P[i * Nk + j] * J->dout[i * d + c];", "acc += J->P[j * Nk + i] * J->dout[i * d + c];"),
+    "dv_uses_transposed_p": ("double w = J->P[i * Nk + j];", "double w = J->P[j * Nk + i];"),
+    # dropout
+    "dropout_scale_missing": ("return byte >= dr->p8 ? 256.0 / (256.0 - (double)dr->p8) : 0.0;",
+                              "return byte >= dr->p8 ? 1.0 : 0.0;"),
+    "dropout_dv_unmasked": ("if (J->Z) w *= J->Z[i * Nk + j];", "/* dV without the mask */"),
+    "dropout_dp_unmasked": ("if (J->Z) acc *= J->Z[i * Nk + j];", "/* dP without the mask */"),
+    "philox_key_not_advanced": ("k[0] += 0x9E3779B9u;", "k[0] += 0u;"),
 }
 
 PINS = [
@@ -43,6 +49,9 @@ PINS = [
     lambda: pins.test_padded_matches_torch_masked_reference(0, True),
     lambda: pins.test_padded_matches_torch_masked_reference(1, False),
     lambda: pins.test_bottom_right_causal_closed_forms(),
+    lambda: pins.test_philox_known_answers(),
+    lambda: pins.test_dropout_matches_torch_masked_reference(True),
+    lambda: pins.test_dropout_is_unbiased(),
 ]
 
 
