@@ -7,10 +7,11 @@ the library's kernels.  There is no fallback: if libfa.so is missing or the
 device is not gfx950 the calls raise.
 
 Names mirror the C ABI: fa_fwd, fa_bwd (and its three stages fa_bwd_preprocess,
-fa_bwd_dkdv, fa_bwd_dq), fa_fwd_padded, fa_bwd_padded, fa_bwd_workspace_size,
-fa_fwd_plan, fa_bwd_plan, fa_status_str.  fwd(), bwd(), fwd_padded() and
-bwd_padded() are conveniences that allocate the outputs (and the backward
-workspace) with torch and call the corresponding entry point.
+fa_bwd_dkdv, fa_bwd_dq), fa_fwd_padded, fa_bwd_padded, fa_fwd_dropout,
+fa_bwd_dropout, fa_bwd_workspace_size, fa_fwd_plan, fa_bwd_plan, fa_status_str.
+fwd(), bwd(), fwd_padded(), bwd_padded(), fwd_dropout() and bwd_dropout() are
+conveniences that allocate the outputs (and the backward workspace) with torch
+and call the corresponding entry point.
 """
 from __future__ import annotations
 
@@ -59,6 +60,12 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, I,
                                     vp, Z, vp]
         L.fa_bwd_padded.restype = I
+        U64, U32 = ctypes.c_uint64, ctypes.c_uint32
+        L.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, F, U64, U32, I, vp]
+        L.fa_fwd_dropout.restype = I
+        L.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, F,
+                                     U64, U32, I, vp, Z, vp]
+        L.fa_bwd_dropout.restype = I
         L.fa_bwd_workspace_size.argtypes = [I, I, I, I]
         L.fa_bwd_workspace_size.restype = Z
         L.fa_fwd_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(fa_plan_t)]
@@ -316,4 +323,76 @@ def bwd_padded(q, k, v, o, dout, lse, seqlens_q=None, seqlens_k=None, causal: bo
         workspace = torch.empty(fa_bwd_workspace_size(B, H, Nq, d), dtype=torch.uint8, device=q.device)
     fa_bwd_padded(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k,
                   default_scale(d) if scale is None else scale, causal, workspace)
+    return dq, dk, dv
+
+
+def dropout_threshold(p: float) -> int:
+    """The 8-bit drop threshold the library uses for probability p: round(256 p)."""
+    return int(round(float(p) * 256.0))
+
+
+def fa_fwd_dropout(q, k, v, o, lse, seqlens_q, seqlens_k, scale: float, causal: bool,
+                   dropout_p: float, seed: int, offset: int, stream=None) -> None:
+    """fa_fwd_padded with dropout on the attention weights (see include/fa.h)."""
+    import torch
+    B, H, Nq, Nk, d = _check_padded(q, k, v)
+    _check_qkv_like("o", o, q)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be contiguous float32 [B, H, Nq] on q's device")
+    rc = lib().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_k, B, q.device),
+                              B, H, Nq, Nk, d, float(scale), int(bool(causal)), float(dropout_p),
+                              int(seed) & ((1 << 64) - 1), int(offset) & 0xFFFFFFFF, _dtype_code(q),
+                              _stream(stream))
+    if rc:
+        raise FaError("fa_fwd_dropout", rc)
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, scale: float,
+                   causal: bool, dropout_p: float, seed: int, offset: int, workspace,
+                   stream=None) -> None:
+    """Backward of fa_fwd_dropout (same dropout_p, seed and offset)."""
+    import torch
+    B, H, Nq, Nk, d = _check_padded(q, k, v)
+    for name, t in (("o", o), ("dout", dout), ("dq", dq)):
+        _check_qkv_like(name, t, q)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_qkv_like(name, t, k)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    rc = lib().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                              _ptr(dk), _ptr(dv), _lens_ptr(seqlens_q, B, q.device),
+                              _lens_ptr(seqlens_k, B, q.device), B, H, Nq, Nk, d, float(scale),
+                              int(bool(causal)), float(dropout_p), int(seed) & ((1 << 64) - 1),
+                              int(offset) & 0xFFFFFFFF, _dtype_code(q), *_ws(workspace, q),
+                              _stream(stream))
+    if rc:
+        raise FaError("fa_bwd_dropout", rc)
+
+
+def fwd_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, seqlens_q=None,
+                seqlens_k=None, causal: bool = False, scale: float | None = None):
+    """Returns (o, lse) with dropout on the attention weights."""
+    import torch
+    B, H, Nq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_dropout(q, k, v, o, lse, seqlens_q, seqlens_k, default_scale(d) if scale is None else scale,
+                   causal, dropout_p, seed, offset)
+    return o, lse
+
+
+def bwd_dropout(q, k, v, o, dout, lse, dropout_p: float, seed: int, offset: int = 0,
+                seqlens_q=None, seqlens_k=None, causal: bool = False, scale: float | None = None,
+                workspace=None):
+    """Returns (dq, dk, dv) of fwd_dropout."""
+    import torch
+    B, H, Nq, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_size(B, H, Nq, d), dtype=torch.uint8, device=q.device)
+    fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k,
+                   default_scale(d) if scale is None else scale, causal, dropout_p, seed, offset,
+                   workspace)
     return dq, dk, dv

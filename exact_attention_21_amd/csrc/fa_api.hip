@@ -35,6 +35,21 @@ int check_device() {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Dropout probability -> 8-bit threshold p8 = round(256 p) in [0, 255]; the
+// kernels keep a pair iff its random byte is >= p8 and scale kept weights by
+// 256 / (256 - p8).  Returns false for p outside [0, 255.5/256).
+bool dropout_spec(float p, uint64_t seed, uint32_t offset, fa::DropoutSpec *d) {
+  if (!std::isfinite(p) || p < 0.f) return false;
+  const long p8 = std::lrint((double)p * 256.0);
+  if (p8 > 255) return false;
+  d->p8 = (uint32_t)p8;
+  d->k0 = (uint32_t)seed;
+  d->k1 = (uint32_t)(seed >> 32);
+  d->offset = offset;
+  d->scale = (float)(256.0 / (256.0 - (double)p8));
+  return true;
+}
+
 fa::SeqShape seq_shape(int H, int Nq, int Nk, const int *lq, const int *lk) {
   fa::SeqShape s;
   s.Nq = Nq;
@@ -78,7 +93,7 @@ const char *fa_status_str(int s) {
     case FA_ERR_WORKSPACE: return "backward workspace too small";
     case FA_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_ARG: return "scale must be finite and > 0; causal must be 0 or 1";
+    case FA_ERR_ARG: return "scale must be finite and > 0; causal must be 0 or 1; dropout_p in [0, 255.5/256)";
     default: return "unknown status";
   }
 }
@@ -108,7 +123,7 @@ namespace {
 
 int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, const int *lq,
              const int *lk, int B, int H, int Nq, int Nk, int d, float scale, int causal,
-             int dtype, void *stream) {
+             float dropout_p, uint64_t seed, uint32_t offset, int dtype, void *stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   fa_plan_t plan;
   int rc = fa_fwd_plan(B, H, Nq, d, causal, dtype, &plan);
@@ -116,12 +131,13 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, c
   rc = check_common(B, H, Nk, d, causal, dtype);
   if (rc) return rc;
   if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  fa::FwdParams p;
+  if (!dropout_spec(dropout_p, seed, offset, &p.drop)) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   if (!aligned4(lq) || !aligned4(lk)) return FA_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
-  fa::FwdParams p;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -142,14 +158,23 @@ extern "C" {
 
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
            int N, int d, float scale, int causal, int dtype, void *stream) {
-  return fwd_impl(q, k, v, o, lse, nullptr, nullptr, B, H, N, N, d, scale, causal, dtype, stream);
+  return fwd_impl(q, k, v, o, lse, nullptr, nullptr, B, H, N, N, d, scale, causal, 0.f, 0, 0, dtype,
+                  stream);
 }
 
 int fa_fwd_padded(const void *q, const void *k, const void *v, void *o, float *lse,
                   const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
                   int d, float scale, int causal, int dtype, void *stream) {
-  return fwd_impl(q, k, v, o, lse, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale, causal, dtype,
-                  stream);
+  return fwd_impl(q, k, v, o, lse, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale, causal, 0.f, 0, 0,
+                  dtype, stream);
+}
+
+int fa_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, float dropout_p, uint64_t seed,
+                   uint32_t offset, int dtype, void *stream) {
+  return fwd_impl(q, k, v, o, lse, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale, causal, dropout_p,
+                  seed, offset, dtype, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
@@ -288,14 +313,15 @@ namespace {
 
 int bwd_impl(const void *q, const void *k, const void *v, const void *o, const void *dout,
              const float *lse, void *dq, void *dk, void *dv, const int *lq, const int *lk, int B,
-             int H, int Nq, int Nk, int d, float scale, int causal, int dtype, void *workspace,
-             size_t workspace_bytes, void *stream) {
+             int H, int Nq, int Nk, int d, float scale, int causal, float dropout_p, uint64_t seed,
+             uint32_t offset, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
   fa::BwdParams p;
   fa_plan_t plan;
   int rc = bwd_setup(B, H, Nq, Nk, lq, lk, d, scale, causal, dtype, workspace, workspace_bytes,
                      &p, &plan);
   if (rc) return rc;
+  if (!dropout_spec(dropout_p, seed, offset, &p.drop)) return FA_ERR_ARG;
   if (!all_aligned({q, k, v, o, dout, lse, dq, dk, dv})) return FA_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
@@ -324,7 +350,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
            void *stream) {
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, H, N, N, d, scale, causal,
-                  dtype, workspace, workspace_bytes, stream);
+                  0.f, 0, 0, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_padded(const void *q, const void *k, const void *v, const void *o, const void *dout,
@@ -332,7 +358,16 @@ int fa_bwd_padded(const void *q, const void *k, const void *v, const void *o, co
                   const int *seqlens_k, int B, int H, int Nq, int Nk, int d, float scale,
                   int causal, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale,
-                  causal, dtype, workspace, workspace_bytes, stream);
+                  causal, 0.f, 0, 0, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                   const float *lse, void *dq, void *dk, void *dv, const int *seqlens_q,
+                   const int *seqlens_k, int B, int H, int Nq, int Nk, int d, float scale,
+                   int causal, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale,
+                  causal, dropout_p, seed, offset, dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

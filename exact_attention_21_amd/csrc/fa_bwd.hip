@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 // ---------------------------------------------------------------------------
 // dQ: query-major pass
 // ---------------------------------------------------------------------------
-template <class T, int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DQ_WAVES_PER_SIMD, BWD_DQ_WAVES_PER_SIMD)))
 void bwd_dq_kernel(BwdParams p) {
   constexpr int BN = 32;                // keys per step
@@ -232,6 +232,10 @@ void bwd_dq_kernel(BwdParams p) {
     // P^T = exp2(scale log2e S - LSE log2e), masked; dS^T = P^T (dP^T - D)
     const int j0 = t * BN;
     const bool need_mask = (CAUSAL && j0 + BN - 1 > wr0 + shift) || (j0 + BN > Lk);
+    // dropout: dP is masked and scaled (dS = P (Z dP - D), Z = keep * 256 / (256 - p8))
+    const uint32_t keep = DROP ? keep_bits_query_major(qrow, j0, hi, (uint32_t)bh, p.drop.offset,
+                                                       p.drop.k0, p.drop.k1, p.drop.p8)
+                               : 0u;
     uint32_t dsk[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -244,7 +248,10 @@ void bwd_dq_kernel(BwdParams p) {
           const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
           pr = key <= lim ? pr : 0.f;
         }
-        v2[e] = pr * (dp[r] - dsum);
+        if constexpr (DROP)
+          v2[e] = pr * (((keep >> r) & 1 ? dp[r] * p.drop.scale : 0.f) - dsum);
+        else
+          v2[e] = pr * (dp[r] - dsum);
       }
       dsk[j] = T::pack(v2[0], v2[1]);
     }
@@ -300,7 +307,7 @@ void bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV: key-major pass
 // ---------------------------------------------------------------------------
-template <class T, int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DKDV_WAVES_PER_SIMD, BWD_DKDV_WAVES_PER_SIMD)))
 void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BM = BWD_DKDV_BM;       // query rows per step
@@ -461,6 +468,10 @@ void bwd_dkdv_kernel(BwdParams p) {
       dp = T::mma(lds_read16(ds + fa), vf[db], dp);
     }
     const bool need_mask = CAUSAL && q0 + shift < kw0 + 31;
+    // dropout: dV takes P * keep (scaled in the epilogue), dS = P (Z dP - D)
+    const uint32_t keep = DROP ? keep_bits_key_major(key, q0, hi, (uint32_t)bh, p.drop.offset,
+                                                     p.drop.k0, p.drop.k1, p.drop.p8)
+                               : 0u;
     uint32_t pk[8], sk[8];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
@@ -474,8 +485,14 @@ void bwd_dkdv_kernel(BwdParams p) {
         // rows past Lq load LSE2 = D = 0 and Q = dO = 0, so they contribute nothing
         float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lq[e]));
         if (need_mask) pr = key <= q0 + qr + e + shift ? pr : 0.f;
-        pv[e] = pr;
-        sv[e] = pr * (dp[r] - dq[e]);
+        if constexpr (DROP) {
+          const bool kept = (keep >> r) & 1;
+          pv[e] = kept ? pr : 0.f;
+          sv[e] = pr * ((kept ? dp[r] * p.drop.scale : 0.f) - dq[e]);
+        } else {
+          pv[e] = pr;
+          sv[e] = pr * (dp[r] - dq[e]);
+        }
       }
       pk[2 * rg] = T::pack(pv[0], pv[1]);
       pk[2 * rg + 1] = T::pack(pv[2], pv[3]);
@@ -528,6 +545,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     uint16_t *dVh = reinterpret_cast<uint16_t *>(p.dv) + koff;
     const bool live = key < Lk;  // padding keys store zeros (their sums are meaningless)
     const float sc = p.scale;
+    const float sd = DROP ? p.drop.scale : 1.f;  // dV = sum (P * keep) dO * 256 / (256 - p8)
 #pragma unroll
     for (int c = 0; c < ND32; ++c)
 #pragma unroll
@@ -537,8 +555,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         if (live) {
           a[0] = T::pack(dkacc[c][4 * rg] * sc, dkacc[c][4 * rg + 1] * sc);
           a[1] = T::pack(dkacc[c][4 * rg + 2] * sc, dkacc[c][4 * rg + 3] * sc);
-          b[0] = T::pack(dvacc[c][4 * rg], dvacc[c][4 * rg + 1]);
-          b[1] = T::pack(dvacc[c][4 * rg + 2], dvacc[c][4 * rg + 3]);
+          b[0] = T::pack(dvacc[c][4 * rg] * sd, dvacc[c][4 * rg + 1] * sd);
+          b[1] = T::pack(dvacc[c][4 * rg + 2] * sd, dvacc[c][4 * rg + 3] * sd);
         }
         *reinterpret_cast<u32x2 *>(dKh + (size_t)key * D + dcol) = a;
         *reinterpret_cast<u32x2 *>(dVh + (size_t)key * D + dcol) = b;
@@ -559,22 +577,30 @@ static hipError_t launch_pre_t(const BwdParams &p, long rows, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class T, int D>
-static hipError_t launch_dq_t(const BwdParams &p, int causal, int grid, hipStream_t st) {
-  if (causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, p);
+template <class T, int D, bool C>
+static hipError_t launch_dq_c(const BwdParams &p, int grid, hipStream_t st) {
+  if (p.drop.p8 != 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, C, true>), dim3(grid), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, C, false>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
+template <class T, int D>
+static hipError_t launch_dq_t(const BwdParams &p, int causal, int grid, hipStream_t st) {
+  return causal ? launch_dq_c<T, D, true>(p, grid, st) : launch_dq_c<T, D, false>(p, grid, st);
+}
 
+template <class T, int D, bool C>
+static hipError_t launch_dkdv_c(const BwdParams &p, int grid, hipStream_t st) {
+  if (p.drop.p8 != 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, C, true>), dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, C, false>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
 template <class T, int D>
 static hipError_t launch_dkdv_t(const BwdParams &p, int causal, int grid, hipStream_t st) {
-  if (causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), dim3(grid), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), dim3(grid), dim3(256), 0, st, p);
-  return hipGetLastError();
+  return causal ? launch_dkdv_c<T, D, true>(p, grid, st) : launch_dkdv_c<T, D, false>(p, grid, st);
 }
 
 hipError_t launch_bwd_pre(const BwdParams &p, int dtype, int d, long rows, hipStream_t st) {

@@ -144,4 +144,88 @@ __device__ __forceinline__ void barrier_only() {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }   // v_log_f32 (base 2)
 
+// ---- dropout mask ------------------------------------------------------------
+// Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw
+// ("Parallel random numbers: as easy as 1, 2, 3", SC'11): ten rounds, each
+// multiplying counter words 0 and 2 by two fixed odd constants into 64-bit
+// products whose halves are permuted and xored with the other counter words and
+// the key; the key advances by a Weyl increment between rounds.  The key is
+// uniform across the wave, so its schedule stays in scalar registers.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    c = u32x4{hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0};
+  }
+  return c;
+}
+
+// 4x4 transpose of words across each group of four consecutive lanes: lane t
+// returns w[s] = (lane s of its group).x[t].  Two butterfly stages: exchange
+// with lane t ^ 1 the registers whose index differs from t in bit 0, then with
+// lane t ^ 2 those differing in bit 1 (DPP quad permutations).
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 x) {
+  const int t = threadIdx.x & 3;
+  auto swap1 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true); };  // [1,0,3,2]
+  auto swap2 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true); };  // [2,3,0,1]
+  const bool odd = t & 1, high = t & 2;
+  const uint32_t p0 = swap1(x[0]), p1 = swap1(x[1]), p2 = swap1(x[2]), p3 = swap1(x[3]);
+  const u32x4 y = {odd ? p1 : x[0], odd ? x[1] : p0, odd ? p3 : x[2], odd ? x[3] : p2};
+  const uint32_t q0 = swap2(y[0]), q1 = swap2(y[1]), q2 = swap2(y[2]), q3 = swap2(y[3]);
+  return u32x4{high ? q2 : y[0], high ? q3 : y[1], high ? y[2] : q0, high ? y[3] : q1};
+}
+
+// 4x4 transpose of bytes inside a lane: y[t] byte s = x[s] byte t.
+__device__ __forceinline__ u32x4 byte_transpose(u32x4 x) {
+  // (x0 b_i, x1 b_i, x0 b_i+1, x1 b_i+1) for i = 0, 2, and the same for x2, x3
+  const uint32_t lo01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
+  const uint32_t hi01 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
+  const uint32_t lo23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  const uint32_t hi23 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  return u32x4{__builtin_amdgcn_perm(lo23, lo01, 0x05040100u), __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+               __builtin_amdgcn_perm(hi23, hi01, 0x05040100u), __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+}
+
+// Keep bits of the 16 (query, key) pairs an MFMA accumulator lane holds, bit r
+// for register r = 4a + b.  A pair (i, j) of head bh is kept iff byte j % 4 of
+// word i % 4 of Philox(counter = (j / 4, i / 4, bh, offset), key) >= p8.
+// Query-major lanes (one query i, keys j0 + 8a + 4hi + b): the lane computes the
+// block of key group j0/4 + 2t + hi (t = i % 4, quad member), and the quad
+// transpose hands every lane word i % 4 of the four blocks it needs.
+__device__ __forceinline__ uint32_t keep_bits_query_major(int i, int j0, int hi, uint32_t bh,
+                                                          uint32_t offset, uint32_t k0,
+                                                          uint32_t k1, uint32_t p8) {
+  const int t = i & 3;
+  const u32x4 r = philox4x32_10(u32x4{(uint32_t)(j0 / 4 + 2 * t + hi), (uint32_t)(i / 4), bh, offset}, k0, k1);
+  const u32x4 w = quad_transpose(r);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bits |= (uint32_t)(((w[a] >> (8 * b)) & 0xFFu) >= p8) << (4 * a + b);
+  return bits;
+}
+// Key-major lanes (one key j, queries i0 + 8a + 4hi + b): the lane computes the
+// block of query group i0/4 + 2t + hi (t = j % 4), gathers byte t' of its four
+// words for each quad member t', and the quad transpose hands lane t the bytes
+// of key offset t for the four query groups.
+__device__ __forceinline__ uint32_t keep_bits_key_major(int j, int i0, int hi, uint32_t bh,
+                                                        uint32_t offset, uint32_t k0,
+                                                        uint32_t k1, uint32_t p8) {
+  const int t = j & 3;
+  const u32x4 r = philox4x32_10(u32x4{(uint32_t)(j / 4), (uint32_t)(i0 / 4 + 2 * t + hi), bh, offset}, k0, k1);
+  const u32x4 w = quad_transpose(byte_transpose(r));
+  uint32_t bits = 0;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bits |= (uint32_t)(((w[a] >> (8 * b)) & 0xFFu) >= p8) << (4 * a + b);
+  return bits;
+}
+
 }  // namespace fa

@@ -84,11 +84,13 @@ static_assert(swz_v_period16<64>() && swz_v_period16<128>(), "V swizzle must rep
 
 }  // namespace
 
-// waves per SIMD: two query blocks per wave need the registers of occupancy 2
-#define FWD_OCC(D, QB) ((QB) == 2 ? 2 : (D) == 64 ? FWD_WAVES_D64 : FWD_WAVES_PER_SIMD)
+// waves per SIMD: two query blocks per wave, or dropout's generator state at
+// d = 128, need the registers of occupancy 2
+#define FWD_OCC(D, QB, DROP) \
+  ((QB) == 2 || ((DROP) && (D) == 128) ? 2 : (D) == 64 ? FWD_WAVES_D64 : FWD_WAVES_PER_SIMD)
 
-template <class T, int D, int QB, bool CAUSAL, bool O_IN_AGPR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FWD_OCC(D, QB), FWD_OCC(D, QB))))
+template <class T, int D, int QB, bool CAUSAL, bool O_IN_AGPR, bool DROP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FWD_OCC(D, QB, DROP), FWD_OCC(D, QB, DROP))))
 void fwd_kernel(FwdParams p) {
   constexpr int BN = FWD_BN;
   constexpr int BM = 128 * QB;          // query rows per workgroup
@@ -248,7 +250,8 @@ void fwd_kernel(FwdParams p) {
   };
   // softmax of one tile: new (lazy) running max, probabilities packed to 16 bits,
   // row sums; returns whether the running max moved (output must be rescaled)
-  auto stage_softmax = [&](f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&alpha)[QB]) {
+  auto stage_softmax = [&](f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&alpha)[QB],
+                           const uint32_t (&keep)[QB]) {
     bool grow_any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -268,7 +271,10 @@ void fwd_kernel(FwdParams p) {
       for (int j = 0; j < 8; ++j) {
         const float e0 = fast_exp2(__builtin_fmaf(s[qb][2 * j], sl2, nm));
         const float e1 = fast_exp2(__builtin_fmaf(s[qb][2 * j + 1], sl2, nm));
-        pk[qb][j] = T::pack(e0, e1);
+        if constexpr (DROP)  // dropped weights leave P V but not the row sum
+          pk[qb][j] = T::pack((keep[qb] >> (2 * j)) & 1 ? e0 : 0.f, (keep[qb] >> (2 * j + 1)) & 1 ? e1 : 0.f);
+        else
+          pk[qb][j] = T::pack(e0, e1);
         ls += e0 + e1;  // row sum from the unrounded probabilities (LSE accuracy)
       }
       lrun[qb] = lrun[qb] * alpha[qb] + ls;
@@ -320,10 +326,17 @@ void fwd_kernel(FwdParams p) {
   auto step = [&](int t, auto slot) {
     constexpr int SL = decltype(slot)::value;
     issue_step(t + 1, std::integral_constant<int, SL ^ 1>{});
+    uint32_t keep[QB] = {};
+    if constexpr (DROP) {  // dropout keep bits of this lane's 16 pairs per query block
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        keep[qb] = keep_bits_query_major(wr0 + qb * 32 + l32, t * BN, hi, (uint32_t)bh, p.drop.offset,
+                                         p.drop.k0, p.drop.k1, p.drop.p8);
+    }
     stage_s(slot, sacc);
     if (needs_mask(t)) apply_mask(t, sacc);
     float alpha[QB];
-    const bool resc = stage_softmax(sacc, pk, alpha);
+    const bool resc = stage_softmax(sacc, pk, alpha, keep);
     if (__builtin_amdgcn_ballot_w64(resc) != 0) rescale_o(alpha);
     stage_pv(slot, pk);
     wait_vmcnt<0>();  // tiles for step t + 1 have landed
@@ -352,7 +365,7 @@ void fwd_kernel(FwdParams p) {
     const int row = wr0 + qb * 32 + l32;
     // padding rows and rows that see no key: O = 0, LSE = -inf
     const bool live = row < Lq && lt > 0.f;
-    const float inv = 1.f / lt;
+    const float inv = (DROP ? p.drop.scale : 1.f) / lt;  // kept weights are scaled by 256 / (256 - p8)
     if (row < Nq) {
 #pragma unroll
       for (int c = 0; c < ND32; ++c)
@@ -377,7 +390,10 @@ void fwd_kernel(FwdParams p) {
 
 template <class T, int D, int QB, bool C>
 static hipError_t launch_fwd_t(const FwdParams &p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR>), dim3(grid), dim3(256), 0, st, p);
+  if (p.drop.p8 != 0)
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, true>), dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, false>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

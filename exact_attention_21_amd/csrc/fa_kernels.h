@@ -47,11 +47,21 @@ __device__ __forceinline__ void seq_lengths(const SeqShape &s, int b, int &Lq, i
   Lk = s.lk ? min(max(s.lk[b], 0), s.Nk) : s.Nk;
 }
 
+// Dropout on the attention weights: pair (i, j) of head bh is kept iff byte
+// j % 4 of word i % 4 of Philox4x32-10(counter (j/4, i/4, bh, offset), key
+// (k0, k1)) is >= p8; kept weights are scaled by `scale` = 256 / (256 - p8).
+// p8 = 0: no dropout (the kernels without dropout are launched).
+struct DropoutSpec {
+  uint32_t p8, k0, k1, offset;
+  float scale;
+};
+
 struct FwdParams {
   const void *q, *k, *v;
   void *o;
   float *lse;
   SeqShape seq;
+  DropoutSpec drop;
   int n_qtiles;     // ceil(Nq / BM)
   int xcd_grouped;  // 1: B*H is a multiple of 8 and heads are grouped per XCD
   float scale_log2; // scale * log2(e)
@@ -81,6 +91,7 @@ struct BwdParams {
   float *dws;       // fp32 [B][H][Nq] workspace: D = rowsum(dO * O)
   float *lse2;      // fp32 [B][H][Nq] workspace: LSE * log2(e) (+inf for rows with LSE = -inf)
   SeqShape seq;
+  DropoutSpec drop;
   int n_qtiles;     // ceil(Nq / BWD_DQ_BM)
   int n_ktiles;     // ceil(Nk / BWD_DKDV_BN)
   int xcd_grouped;

@@ -41,6 +41,7 @@
 #define FA_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -58,7 +59,7 @@ typedef enum {
   FA_ERR_WORKSPACE = 6, /* backward workspace too small */
   FA_ERR_DEVICE = 7,    /* current device is not gfx950, or no device */
   FA_ERR_LAUNCH = 8,    /* the HIP runtime rejected a kernel launch */
-  FA_ERR_ARG = 9        /* scale not finite and positive, or causal not 0/1 */
+  FA_ERR_ARG = 9        /* scale not finite and positive, causal not 0/1, or dropout_p out of range */
 } fa_status_t;
 
 /*
@@ -152,6 +153,36 @@ int fa_bwd_padded(const void *q, const void *k, const void *v, const void *o,
                   const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
                   int d, float scale, int causal, int dtype, void *workspace,
                   size_t workspace_bytes, void *stream);
+
+/*
+ * Dropout on the attention weights ("MHA tuning, part 1", section "notes in
+ * practice": the dropout mask is generated block by block inside the fused
+ * computation, and the backward regenerates the same mask instead of storing
+ * it).  Arguments as for fa_fwd_padded / fa_bwd_padded, plus:
+ *   dropout_p  drop probability in [0, 1), quantised to p8 = round(256 p),
+ *              which must be <= 255 (else FA_ERR_ARG); p8 = 0 is no dropout;
+ *   seed       64-bit key of the generator; offset: 32-bit stream offset, so
+ *              successive calls (layers, steps) can use independent masks.
+ * Pair (i, j) of head bh = b*H + h (i, j indices within the head) is kept iff
+ * byte (j mod 4) of word (i mod 4) of Philox4x32-10 (Salmon, Moraes, Dror,
+ * Shaw, SC'11) at counter (j/4, i/4, bh, offset) with key (seed low, seed high
+ * 32 bits) is >= p8; kept weights are scaled by 256 / (256 - p8):
+ *   O_i = sum_j P_ij Z_ij V_j,  Z_ij = keep_ij * 256 / (256 - p8),
+ * with P (and LSE) the softmax before dropout.  The backward must be called
+ * with the same dropout_p, seed and offset as the forward; its gradients are
+ * those of this O (dV = (P Z)^T dO, dS = P (Z (dO V^T) - D)).  Deterministic:
+ * the same arguments give the same mask and bitwise the same outputs.
+ */
+int fa_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, float dropout_p, uint64_t seed,
+                   uint32_t offset, int dtype, void *stream);
+int fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o,
+                   const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                   const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, float dropout_p, uint64_t seed,
+                   uint32_t offset, int dtype, void *workspace, size_t workspace_bytes,
+                   void *stream);
 
 /* Launch plan of a forward call (host-only, no GPU needed). */
 typedef struct {
