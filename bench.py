@@ -132,8 +132,8 @@ def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
 def sweep(fa, device, steps, warmup):
     """Forward and backward timings over the other configurations of the workload
     family (sequence-length sweep at 32768 tokens per batch, the d=64 variant, the
-    non-causal 4096 forward, the 4096 backward, a variable-length causal batch and a
-    cross-attention shape).  Inputs are seeded N(0,1) draws made on the device
+    non-causal 4096 forward, the 4096 backward, a variable-length causal batch, a
+    cross-attention shape and a dropout workload).  Inputs are seeded N(0,1) draws made on the device
     (timing only; parity is the tests' job).  Padded workloads count FLOP over the
     visible pairs only: 4 d per pair forward, 2.5x that backward."""
     import torch
@@ -145,7 +145,8 @@ def sweep(fa, device, steps, warmup):
             continue  # c1 is the oracle-sized case; c3 is the headline above
         B, H, N, d, causal = c["B"], c["H"], c["N"], c["d"], c["causal"]
         Nk = c.get("Nk", N)
-        padded = "len_lo" in c or Nk != N
+        drop = c.get("dropout", 0.0)
+        padded = "len_lo" in c or Nk != N or drop > 0
         tdt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float16
         gen = torch.Generator(device=device).manual_seed(c["seed"])
         draw = lambda n: torch.randn((B, H, n, d), generator=gen, device=device,
@@ -166,13 +167,18 @@ def sweep(fa, device, steps, warmup):
             e = ev[i - warmup] if i >= warmup else None
             if e:
                 e[0].record(stream)
-            if padded:
+            if drop > 0:
+                fa.fa_fwd_dropout(q, k, v, o, lse, lq, lk, scale, causal, drop, c["seed"], i, stream)
+            elif padded:
                 fa.fa_fwd_padded(q, k, v, o, lse, lq, lk, scale, causal, stream)
             else:
                 fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
             if e:
                 e[1].record(stream)
-            if padded:
+            if drop > 0:
+                fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, lq, lk, scale, causal, drop, c["seed"], i,
+                                  ws, stream)
+            elif padded:
                 fa.fa_bwd_padded(q, k, v, o, do, lse, dq, dk, dv, lq, lk, scale, causal, ws, stream)
             else:
                 fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, ws, stream)
@@ -190,6 +196,7 @@ def sweep(fa, device, steps, warmup):
         fms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
         bms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
         res[name] = {"B": B, "H": H, "N": N, "Nk": Nk, "d": d, "dtype": c["dtype"], "causal": causal,
+                     "dropout": drop,
                      "lengths": None if lens is None else [int(x) for x in lens],
                      "fwd_ms": fms, "fwd_tflops": f_fwd / (fms * 1e-3) / 1e12,
                      "bwd_ms": bms, "bwd_tflops": f_bwd / (bms * 1e-3) / 1e12}

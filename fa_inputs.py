@@ -93,4 +93,6 @@ CONFIGS = {
                                                 seed=BASE_SEED + 61, bwd=True, len_lo=512, len_hi=4096),
     "p2_cross_q4096_k16384_d128_bf16": dict(B=2, H=16, N=4096, Nk=16384, d=128, dtype="bf16",
                                             causal=False, seed=BASE_SEED + 62, bwd=True),
+    "p3_dropout10_causal_n4096_d128_bf16": dict(B=8, H=16, N=4096, d=128, dtype="bf16", causal=True,
+                                                seed=BASE_SEED + 63, bwd=True, dropout=0.1),
 }
