@@ -8,10 +8,11 @@ device is not gfx950 the calls raise.
 
 Names mirror the C ABI: fa_fwd, fa_bwd (and its three stages fa_bwd_preprocess,
 fa_bwd_dkdv, fa_bwd_dq), fa_fwd_padded, fa_bwd_padded, fa_fwd_dropout,
-fa_bwd_dropout, fa_bwd_workspace_size, fa_fwd_plan, fa_bwd_plan, fa_status_str.
-fwd(), bwd(), fwd_padded(), bwd_padded(), fwd_dropout() and bwd_dropout() are
-conveniences that allocate the outputs (and the backward workspace) with torch
-and call the corresponding entry point.
+fa_bwd_dropout, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size,
+fa_bwd_workspace_size, fa_fwd_plan, fa_bwd_plan, fa_status_str.
+fwd(), bwd(), fwd_padded(), bwd_padded(), fwd_dropout(), bwd_dropout() and
+fwd_splitkv() are conveniences that allocate the outputs (and workspaces) with
+torch and call the corresponding entry point.
 """
 from __future__ import annotations
 
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, F,
                                      U64, U32, I, vp, Z, vp]
         L.fa_bwd_dropout.restype = I
+        L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, I, vp, Z, vp]
+        L.fa_fwd_splitkv.restype = I
+        L.fa_fwd_splitkv_workspace_size.argtypes = [I, I, I, I, I]
+        L.fa_fwd_splitkv_workspace_size.restype = Z
         L.fa_bwd_workspace_size.argtypes = [I, I, I, I]
         L.fa_bwd_workspace_size.restype = Z
         L.fa_fwd_plan.argtypes = [I, I, I, I, I, I, ctypes.POINTER(fa_plan_t)]
@@ -396,3 +401,40 @@ def bwd_dropout(q, k, v, o, dout, lse, dropout_p: float, seed: int, offset: int 
                    default_scale(d) if scale is None else scale, causal, dropout_p, seed, offset,
                    workspace)
     return dq, dk, dv
+
+
+def fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d) -> int:
+    return int(lib().fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, seqlens_q, seqlens_k, scale: float, causal: bool, workspace,
+                   stream=None) -> None:
+    """fa_fwd_padded's result computed split over key blocks (few queries, long K/V)."""
+    import torch
+    B, H, Nq, Nk, d = _check_padded(q, k, v)
+    _check_qkv_like("o", o, q)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be contiguous float32 [B, H, Nq] on q's device")
+    rc = lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_k, B, q.device),
+                              B, H, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q),
+                              *_ws(workspace, q), _stream(stream))
+    if rc:
+        raise FaError("fa_fwd_splitkv", rc)
+
+
+def fwd_splitkv(q, k, v, seqlens_q=None, seqlens_k=None, causal: bool = False,
+                scale: float | None = None, workspace=None):
+    """Returns (o, lse) like fwd_padded, computed split over key blocks."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d), dtype=torch.uint8,
+                                device=q.device)
+    fa_fwd_splitkv(q, k, v, o, lse, seqlens_q, seqlens_k, default_scale(d) if scale is None else scale,
+                   causal, workspace)
+    return o, lse

@@ -78,6 +78,31 @@ int fwd_qb(int N, int d) { return d == 128 ? FWD_QB_D128 : (N > 128 ? FWD_QB_D64
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Key chunks of the split forward: enough workgroups to fill the GPU (about
+// 1024), at least 256 keys per chunk, chunk a multiple of two key tiles.
+struct SplitPlan {
+  int bm, n_qtiles, nsplit, chunk;
+};
+SplitPlan split_plan(int B, int H, int Nq, int Nk, int d) {
+  SplitPlan sp;
+  sp.bm = 128 * (d == 128 ? FWD_QB_D128 : 1);
+  sp.n_qtiles = (Nq + sp.bm - 1) / sp.bm;
+  const long long units = (long long)B * H * sp.n_qtiles;
+  long long want = (1024 + units - 1) / units;
+  const long long most = ((long long)Nk + 255) / 256;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  const long long tiles2 = 2LL * fa::FWD_BN;
+  sp.chunk = (int)((((long long)Nk + want - 1) / want + tiles2 - 1) / tiles2 * tiles2);
+  sp.nsplit = (int)(((long long)Nk + sp.chunk - 1) / sp.chunk);
+  return sp;
+}
+
+size_t split_workspace_bytes(int B, int H, int Nq, int d, const SplitPlan &sp) {
+  const size_t rows = (size_t)B * H * sp.nsplit * Nq;
+  return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,6 +157,7 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, c
   if (rc) return rc;
   if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
   fa::FwdParams p;
+  std::memset(&p, 0, sizeof p);
   if (!dropout_spec(dropout_p, seed, offset, &p.drop)) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
@@ -175,6 +201,55 @@ int fa_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *
                    uint32_t offset, int dtype, void *stream) {
   return fwd_impl(q, k, v, o, lse, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale, causal, dropout_p,
                   seed, offset, dtype, stream);
+}
+
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d) {
+  if (check_common(B, H, Nq, d, 0, FA_BF16) != FA_OK || check_common(B, H, Nk, d, 0, FA_BF16) != FA_OK)
+    return 0;
+  return split_workspace_bytes(B, H, Nq, d, split_plan(B, H, Nq, Nk, d));
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, int dtype, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+  int rc = check_common(B, H, Nq, d, causal, dtype);
+  if (rc) return rc;
+  rc = check_common(B, H, Nk, d, causal, dtype);
+  if (rc) return rc;
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  const SplitPlan sp = split_plan(B, H, Nq, Nk, d);
+  const long long grid = (long long)sp.n_qtiles * sp.nsplit * B * H;
+  if (grid > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  if (!aligned4(seqlens_q) || !aligned4(seqlens_k)) return FA_ERR_ALIGN;
+  if (workspace_bytes < split_workspace_bytes(B, H, Nq, d, sp)) return FA_ERR_WORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+  fa::FwdParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.seq = seq_shape(H, Nq, Nk, seqlens_q, seqlens_k);
+  p.n_qtiles = sp.n_qtiles;
+  p.xcd_grouped = 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.nsplit = sp.nsplit;
+  p.chunk = sp.chunk;
+  char *ws = static_cast<char *>(workspace);
+  const size_t prows = (size_t)B * H * sp.nsplit * Nq;
+  p.opart = reinterpret_cast<float *>(ws);
+  p.lpart = reinterpret_cast<float *>(ws + align256(prows * d * sizeof(float)));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = fa::launch_fwd_split(p, dtype, d, causal, (int)grid, st);
+  if (e == hipSuccess) e = fa::launch_fwd_combine(p, dtype, d, (long)B * H * Nq, st);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {

@@ -89,7 +89,7 @@ static_assert(swz_v_period16<64>() && swz_v_period16<128>(), "V swizzle must rep
 #define FWD_OCC(D, QB, DROP) \
   ((QB) == 2 || ((DROP) && (D) == 128) ? 2 : (D) == 64 ? FWD_WAVES_D64 : FWD_WAVES_PER_SIMD)
 
-template <class T, int D, int QB, bool CAUSAL, bool O_IN_AGPR, bool DROP>
+template <class T, int D, int QB, bool CAUSAL, bool O_IN_AGPR, bool DROP, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FWD_OCC(D, QB, DROP), FWD_OCC(D, QB, DROP))))
 void fwd_kernel(FwdParams p) {
   constexpr int BN = FWD_BN;
@@ -119,10 +119,12 @@ void fwd_kernel(FwdParams p) {
   const int g = lane >> 4, s16 = lane & 15;
 
   // ---- which (head, query tile) this workgroup computes
+  static_assert(!(SPLIT && DROP), "the split forward has no dropout");
   int bh, qt;
+  const int split = SPLIT ? (int)(blockIdx.x % (unsigned)p.nsplit) : 0;
   {
     const int nq = p.n_qtiles;
-    const int bid = blockIdx.x;
+    const int bid = SPLIT ? (int)(blockIdx.x / (unsigned)p.nsplit) : (int)blockIdx.x;
     int r;
     if (p.xcd_grouped) {  // heads of one XCD (bid % 8) run together: K/V stay in its L2
       const int x = bid & 7, kk = bid >> 3;
@@ -150,6 +152,9 @@ void fwd_kernel(FwdParams p) {
   // keys the workgroup's rows can see (none if all its rows are padding)
   const int kend = i0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, i0 + BM + shift)) : Lk;
   const int nt = (kend + BN - 1) / BN;
+  // key tiles of this workgroup: all of them, or one chunk of the split forward
+  const int t_beg = SPLIT ? min(nt, split * (p.chunk / BN)) : 0;
+  const int t_end = SPLIT ? min(nt, t_beg + p.chunk / BN) : nt;
   const float sl2 = p.scale_log2;
 
   // ---- K/V tile DMA: this lane's share of block (w * BPW + j) of a tile
@@ -164,7 +169,7 @@ void fwd_kernel(FwdParams p) {
   auto issue_tile = [&](const __amdgpu_buffer_rsrc_t &rsrc, int t, char *slot,
                         const uint32_t (&offs)[BPW]) {
     // tiles outside [0, nt) load as zeros (offset past the resource end)
-    const bool ok = t >= 0 && t < nt;
+    const bool ok = t >= t_beg && t < t_end;
     const uint32_t base = ok ? (uint32_t)t * TB : 0x80000000u;
 #pragma unroll
     for (int j = 0; j < BPW; ++j) dma16(rsrc, slot + (w * BPW + j) * 1024, base + offs[j]);
@@ -345,20 +350,22 @@ void fwd_kernel(FwdParams p) {
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
-  issue_step(0, S0{});
+  issue_step(t_beg, S0{});
   wait_vmcnt<0>();
   barrier_only();
-  int t = 0;
-  for (; t + 1 < nt; t += 2) {  // tile t lives in slot t & 1
+  int t = t_beg;
+  for (; t + 1 < t_end; t += 2) {  // tile t lives in slot (t - t_beg) & 1
     step(t, S0{});
     step(t + 1, S1{});
   }
-  if (t < nt) step(t, S0{});
+  if (t < t_end) step(t, S0{});
   wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
-  // ---- epilogue: O = acc / l (rounded to 16 bits), LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = acc / l (rounded to 16 bits), LSE = (m + log2 l) ln 2;
+  // the split forward writes this chunk's O (fp32) and LSE to the partials
   uint16_t *Oh = reinterpret_cast<uint16_t *>(p.o) + qoff;
   float *Lh = p.lse + (size_t)bh * Nq;
+  const size_t pbase = SPLIT ? ((size_t)bh * p.nsplit + split) * Nq : 0;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = lrun[qb] + xhalf(lrun[qb]);
@@ -366,7 +373,21 @@ void fwd_kernel(FwdParams p) {
     // padding rows and rows that see no key: O = 0, LSE = -inf
     const bool live = row < Lq && lt > 0.f;
     const float inv = (DROP ? p.drop.scale : 1.f) / lt;  // kept weights are scaled by 256 / (256 - p8)
-    if (row < Nq) {
+    if (SPLIT && row < Nq) {
+#pragma unroll
+      for (int c = 0; c < ND32; ++c)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int dcol = c * 32 + 8 * rg + 4 * hi;
+          f32x4 st = {0.f, 0.f, 0.f, 0.f};
+          if (live)
+            st = f32x4{oacc[qb][c][4 * rg] * inv, oacc[qb][c][4 * rg + 1] * inv,
+                       oacc[qb][c][4 * rg + 2] * inv, oacc[qb][c][4 * rg + 3] * inv};
+          *reinterpret_cast<f32x4 *>(p.opart + (pbase + row) * D + dcol) = st;
+        }
+      if (hi == 0)
+        p.lpart[pbase + row] = live ? (mrun[qb] + fast_log2(lt)) * 0.69314718055994531f : -__builtin_inff();
+    } else if (!SPLIT && row < Nq) {
 #pragma unroll
       for (int c = 0; c < ND32; ++c)
 #pragma unroll
@@ -385,16 +406,91 @@ void fwd_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Merge of the split forward's partials: per query row, with L_s the chunks'
+// log-sum-exps and O_s their normalised outputs, LSE = log sum_s exp(L_s) and
+// O = sum_s exp(L_s - LSE) O_s -- the block-merge rule of the handbook's
+// engineering-implementation pseudocode, applied across chunks.  Chunks that see
+// no key have L_s = -inf and weight 0; a row with no visible key at all gets
+// O = 0, LSE = -inf.  One wave per row, D / 64 output columns per lane.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(const float *__restrict__ opart,
+                                                          const float *__restrict__ lpart,
+                                                          uint16_t *__restrict__ o,
+                                                          float *__restrict__ lse, int nsplit,
+                                                          int Nq, long rows) {
+  constexpr int CPL = D / 64;  // columns per lane
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;  // whole waves exit together
+  const long bh = row / Nq, i = row % Nq;
+  const float *ls = lpart + (size_t)bh * nsplit * Nq + i;  // stride Nq between chunks
+  float m = -__builtin_inff();
+  for (int s = lane; s < nsplit; s += 64) m = fmaxf(m, ls[(size_t)s * Nq]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  float acc[CPL] = {};
+  float wsum = 0.f;
+  if (m != -__builtin_inff()) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float w = __expf(ls[(size_t)s * Nq] - m);  // 0 for chunks with L_s = -inf
+      wsum += w;
+      const float *os = opart + (((size_t)bh * nsplit + s) * Nq + i) * D + lane * CPL;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] += w * os[c];
+    }
+  }
+  const bool live = wsum > 0.f;
+  uint16_t *orow = o + (size_t)row * D + lane * CPL;
+  if constexpr (CPL == 2) {
+    *reinterpret_cast<uint32_t *>(orow) = live ? T::pack(acc[0] / wsum, acc[1] / wsum) : 0u;
+  } else {
+    const uint32_t pk = live ? T::pack(acc[0] / wsum, 0.f) : 0u;
+    orow[0] = (uint16_t)(pk & 0xFFFFu);
+  }
+  if (lane == 0) lse[row] = live ? m + __logf(wsum) : -__builtin_inff();
+}
+
+// ---------------------------------------------------------------------------
 // instantiation table
 // ---------------------------------------------------------------------------
 
 template <class T, int D, int QB, bool C>
 static hipError_t launch_fwd_t(const FwdParams &p, int grid, hipStream_t st) {
   if (p.drop.p8 != 0)
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, true>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, true, false>), dim3(grid), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, false>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, false, false>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
+}
+
+template <class T, int D, bool C>
+static hipError_t launch_split_t(const FwdParams &p, int grid, hipStream_t st) {
+  constexpr int QB = D == 128 ? FWD_QB_D128 : 1;
+  hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, false, true>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_split(const FwdParams &p, int dtype, int d, int causal, int grid,
+                            hipStream_t st) {
+  if (dtype == 1)
+    return d == 128 ? (causal ? launch_split_t<BF16, 128, true>(p, grid, st) : launch_split_t<BF16, 128, false>(p, grid, st))
+                    : (causal ? launch_split_t<BF16, 64, true>(p, grid, st) : launch_split_t<BF16, 64, false>(p, grid, st));
+  return d == 128 ? (causal ? launch_split_t<F16, 128, true>(p, grid, st) : launch_split_t<F16, 128, false>(p, grid, st))
+                  : (causal ? launch_split_t<F16, 64, true>(p, grid, st) : launch_split_t<F16, 64, false>(p, grid, st));
+}
+
+template <class T, int D>
+static hipError_t launch_combine_t(const FwdParams &p, long rows, hipStream_t st) {
+  const int grid = (int)((rows + 3) / 4);
+  hipLaunchKernelGGL((fwd_combine_kernel<T, D>), dim3(grid), dim3(256), 0, st, p.opart, p.lpart,
+                     reinterpret_cast<uint16_t *>(p.o), p.lse, p.nsplit, p.seq.Nq, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_combine(const FwdParams &p, int dtype, int d, long rows, hipStream_t st) {
+  if (dtype == 1) return d == 128 ? launch_combine_t<BF16, 128>(p, rows, st) : launch_combine_t<BF16, 64>(p, rows, st);
+  return d == 128 ? launch_combine_t<F16, 128>(p, rows, st) : launch_combine_t<F16, 64>(p, rows, st);
 }
 
 hipError_t launch_fwd(const FwdParams &p, int dtype, int d, int causal, int qb, int grid,

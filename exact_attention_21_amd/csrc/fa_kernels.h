@@ -62,6 +62,11 @@ struct FwdParams {
   float *lse;
   SeqShape seq;
   DropoutSpec drop;
+  // split over key blocks: workgroup (head, query tile, split s) covers keys
+  // [s * chunk, (s + 1) * chunk) and writes its normalised partial output and
+  // LSE to opart [B*H][nsplit][Nq][d] / lpart [B*H][nsplit][Nq] (fp32)
+  int nsplit, chunk;
+  float *opart, *lpart;
   int n_qtiles;     // ceil(Nq / BM)
   int xcd_grouped;  // 1: B*H is a multiple of 8 and heads are grouped per XCD
   float scale_log2; // scale * log2(e)
@@ -110,5 +115,10 @@ hipError_t launch_bwd_dkdv(const BwdParams &p, int dtype, int d, int causal, int
 
 hipError_t launch_fwd(const FwdParams &p, int dtype, int d, int causal, int qb, int grid,
                       hipStream_t st);
+// split-over-keys forward (grid = n_qtiles * nsplit * B * H), then the merge of
+// the partials into o and lse (one wave per query row)
+hipError_t launch_fwd_split(const FwdParams &p, int dtype, int d, int causal, int grid,
+                            hipStream_t st);
+hipError_t launch_fwd_combine(const FwdParams &p, int dtype, int d, long rows, hipStream_t st);
 
 }  // namespace fa

@@ -184,6 +184,29 @@ int fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o,
                    uint32_t offset, int dtype, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/*
+ * Forward split over key blocks, for few queries over a long K/V (decoding
+ * against a key/value cache; the xformers page's decoding benchmark and the
+ * first-token latency scenario of "Flash Attention application").  The keys
+ * of each (batch, head, query tile) are cut into chunks that run as separate
+ * workgroups, so that B*H*ceil(Nq/128) small does not leave the GPU idle; each
+ * chunk writes its normalised partial output and log-sum-exp, and a second
+ * kernel merges the chunks with the LSE merge rule of the handbook's
+ * engineering-implementation pseudocode:
+ *   LSE = log sum_c exp(L_c),  O = sum_c exp(L_c - LSE) O_c.
+ * Arguments and results as for fa_fwd_padded (the same function: padded
+ * lengths, N_q != N_k, causal aligned to the last query and key); the
+ * workspace must hold fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d) bytes
+ * (16-byte aligned; fp32 partials), its contents on entry do not matter.
+ * Results are deterministic but not bitwise equal to fa_fwd_padded's (the
+ * additions happen in another order).  Forward only.
+ */
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d);
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, int dtype, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
 /* Launch plan of a forward call (host-only, no GPU needed). */
 typedef struct {
   int block_m;          /* query rows per workgroup */
