@@ -129,11 +129,50 @@ def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
     return total
 
 
+def decode_timing(fa, c, q, k, v, steps, warmup):
+    """Decode-shaped forward (few queries, long K/V): fa_fwd_splitkv against the
+    unsplit fa_fwd_padded on the same inputs.  The bound is HBM: bytes = Q, K, V
+    read and O, LSE written."""
+    import torch
+    stream = torch.cuda.current_stream()
+    B, H, N, d, causal = c["B"], c["H"], c["N"], c["d"], c["causal"]
+    Nk = c["Nk"]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws = torch.empty(fa.fa_fwd_splitkv_workspace_size(B, H, N, Nk, d), dtype=torch.uint8, device=q.device)
+    scale = 1 / math.sqrt(d)
+
+    def timed(fn):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(warmup + steps):
+            e = ev[i - warmup] if i >= warmup else None
+            if e:
+                e[0].record(stream)
+            fn()
+            if e:
+                e[1].record(stream)
+        torch.cuda.synchronize()
+        return sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+
+    split_ms = timed(lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, None, None, scale, causal, ws, stream))
+    plain_ms = timed(lambda: fa.fa_fwd_padded(q, k, v, o, lse, None, None, scale, causal, stream))
+    nbytes = 2.0 * B * H * d * (2 * N + 2 * Nk) + 4.0 * B * H * N
+    flop = 4.0 * d * B * H * visible_pairs(N, Nk, causal)
+    r = {"B": B, "H": H, "N": N, "Nk": Nk, "d": d, "dtype": c["dtype"], "causal": causal,
+         "fwd_ms": split_ms, "fwd_tflops": flop / (split_ms * 1e-3) / 1e12,
+         "hbm_bytes": nbytes, "hbm_gbps": nbytes / (split_ms * 1e-3) / 1e9,
+         "hbm_frac_of_8tbps": nbytes / (split_ms * 1e-3) / 8e12, "unsplit_fwd_ms": plain_ms}
+    log(f"[bench] sweep {c.get('name', '')}decode B={B} H={H} Nq={N} Nk={Nk}: split-KV {split_ms:.3f} ms "
+        f"({r['hbm_gbps']:.0f} GB/s, {100 * r['hbm_frac_of_8tbps']:.0f} % of 8 TB/s); unsplit {plain_ms:.3f} ms")
+    return r
+
+
 def sweep(fa, device, steps, warmup):
     """Forward and backward timings over the other configurations of the workload
     family (sequence-length sweep at 32768 tokens per batch, the d=64 variant, the
     non-causal 4096 forward, the 4096 backward, a variable-length causal batch, a
-    cross-attention shape and a dropout workload).  Inputs are seeded N(0,1) draws made on the device
+    cross-attention shape, a dropout workload and a decode shape timed through the
+    split-over-keys forward).  Inputs are seeded N(0,1) draws made on the device
     (timing only; parity is the tests' job).  Padded workloads count FLOP over the
     visible pairs only: 4 d per pair forward, 2.5x that backward."""
     import torch
@@ -153,6 +192,10 @@ def sweep(fa, device, steps, warmup):
                                      dtype=torch.float32).to(tdt)
         q, do = draw(N), draw(N)
         k, v = draw(Nk), draw(Nk)
+        if c.get("splitkv"):
+            res[name] = decode_timing(fa, c, q, k, v, steps, warmup)
+            del q, k, v, do
+            continue
         lens = None
         if "len_lo" in c:
             lens = fa_inputs.seq_lengths(B, c["len_lo"], c["len_hi"], c["seed"])

@@ -78,8 +78,9 @@ int fwd_qb(int N, int d) { return d == 128 ? FWD_QB_D128 : (N > 128 ? FWD_QB_D64
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Key chunks of the split forward: enough workgroups to fill the GPU (about
-// 1024), at least 256 keys per chunk, chunk a multiple of two key tiles.
+// Key chunks of the split forward: about 4096 workgroups (the GPU holds 768 at
+// once, so the last partial round of workgroups costs little), at least 256
+// keys per chunk, chunk a multiple of two key tiles.
 struct SplitPlan {
   int bm, n_qtiles, nsplit, chunk;
 };
@@ -88,7 +89,7 @@ SplitPlan split_plan(int B, int H, int Nq, int Nk, int d) {
   sp.bm = 128 * (d == 128 ? FWD_QB_D128 : 1);
   sp.n_qtiles = (Nq + sp.bm - 1) / sp.bm;
   const long long units = (long long)B * H * sp.n_qtiles;
-  long long want = (1024 + units - 1) / units;
+  long long want = (4096 + units - 1) / units;
   const long long most = ((long long)Nk + 255) / 256;
   if (want > most) want = most;
   if (want < 1) want = 1;

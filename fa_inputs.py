@@ -95,4 +95,8 @@ CONFIGS = {
                                             causal=False, seed=BASE_SEED + 62, bwd=True),
     "p3_dropout10_causal_n4096_d128_bf16": dict(B=8, H=16, N=4096, d=128, dtype="bf16", causal=True,
                                                 seed=BASE_SEED + 63, bwd=True, dropout=0.1),
+    # decoding one token per sequence against a 16k key/value cache
+    "p4_decode_b32_h32_q1_k16384_d128_bf16": dict(B=32, H=32, N=1, Nk=16384, d=128, dtype="bf16",
+                                                  causal=True, seed=BASE_SEED + 64, bwd=False,
+                                                  splitkv=True),
 }
