@@ -236,6 +236,13 @@ void bwd_dq_kernel(BwdParams p) {
     const uint32_t keep = DROP ? keep_bits_query_major(qrow, j0, hi, (uint32_t)bh, p.drop.offset,
                                                        p.drop.k0, p.drop.k1, p.drop.p8)
                                : 0u;
+    if (need_mask) {  // a separate block: most steps skip it
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[r] = key <= lim ? s[r] : -__builtin_inff();
+      }
+    }
     uint32_t dsk[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -243,11 +250,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * j + e;
-        float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lse2));
-        if (need_mask) {
-          const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          pr = key <= lim ? pr : 0.f;
-        }
+        const float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lse2));  // masked: exp2(-inf) = 0
         if constexpr (DROP)
           v2[e] = pr * (((keep >> r) & 1 ? dp[r] * p.drop.scale : 0.f) - dsum);
         else
@@ -472,6 +475,13 @@ void bwd_dkdv_kernel(BwdParams p) {
     const uint32_t keep = DROP ? keep_bits_key_major(key, q0, hi, (uint32_t)bh, p.drop.offset,
                                                      p.drop.k0, p.drop.k1, p.drop.p8)
                                : 0u;
+    if (need_mask) {  // a separate block: most steps skip it
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        s[r] = key <= qrow + shift ? s[r] : -__builtin_inff();
+      }
+    }
     uint32_t pk[8], sk[8];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
@@ -483,8 +493,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rg + e;
         // rows past Lq load LSE2 = D = 0 and Q = dO = 0, so they contribute nothing
-        float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lq[e]));
-        if (need_mask) pr = key <= q0 + qr + e + shift ? pr : 0.f;
+        const float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lq[e]));  // masked: exp2(-inf) = 0
         if constexpr (DROP) {
           const bool kept = (keep >> r) & 1;
           pv[e] = kept ? pr : 0.f;
