@@ -167,7 +167,7 @@ def decode_timing(fa, c, q, k, v, steps, warmup):
     return r
 
 
-def sweep(fa, device, steps, warmup):
+def sweep(fa, device, steps, warmup, only=None):
     """Forward and backward timings over the other configurations of the workload
     family (sequence-length sweep at 32768 tokens per batch, the d=64 variant, the
     non-causal 4096 forward, the 4096 backward, a variable-length causal batch, a
@@ -182,6 +182,8 @@ def sweep(fa, device, steps, warmup):
     for name, c in fa_inputs.CONFIGS.items():
         if name.startswith("c1_") or name.startswith("c3_"):
             continue  # c1 is the oracle-sized case; c3 is the headline above
+        if only and only not in name:
+            continue
         B, H, N, d, causal = c["B"], c["H"], c["N"], c["d"], c["causal"]
         Nk = c.get("Nk", N)
         drop = c.get("dropout", 0.0)
@@ -273,6 +275,7 @@ def main():
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (diagnostics)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the other configurations' timings")
     ap.add_argument("--sweep-only", action="store_true", help="time only the other configurations")
+    ap.add_argument("--only", default=None, help="with --sweep-only: configurations whose name contains this")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -292,7 +295,7 @@ def main():
         return
 
     if args.sweep_only:
-        print(json.dumps({"sweep": sweep(fa, device, args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"sweep": sweep(fa, device, args.steps, args.warmup, args.only)}), flush=True)
         return
 
     w = WORKLOAD

@@ -59,6 +59,10 @@ static_assert(swz_period16<64>() && swz_period16<128>(), "swizzles must repeat e
 
 }  // namespace
 
+// waves per SIMD of the two passes (occupancy targets; d = 64 needs fewer registers)
+#define BWD_DQ_OCC(D, DROP) ((D) == 64 && !(DROP) ? BWD_DQ_WAVES_D64 : BWD_DQ_WAVES_PER_SIMD)
+#define BWD_DKDV_OCC(D, DROP) ((D) == 64 && !(DROP) ? BWD_DKDV_WAVES_D64 : BWD_DKDV_WAVES_PER_SIMD)
+
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O) and LSE * log2(e).  16 threads per row.
 // ---------------------------------------------------------------------------
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 // dQ: query-major pass
 // ---------------------------------------------------------------------------
 template <class T, int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DQ_WAVES_PER_SIMD, BWD_DQ_WAVES_PER_SIMD)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DQ_OCC(D, DROP), BWD_DQ_OCC(D, DROP))))
 void bwd_dq_kernel(BwdParams p) {
   constexpr int BN = 32;                // keys per step
   constexpr int BM = BWD_DQ_BM;         // query rows per workgroup (32 per wave)
@@ -311,7 +315,7 @@ void bwd_dq_kernel(BwdParams p) {
 // dK, dV: key-major pass
 // ---------------------------------------------------------------------------
 template <class T, int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DKDV_WAVES_PER_SIMD, BWD_DKDV_WAVES_PER_SIMD)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DKDV_OCC(D, DROP), BWD_DKDV_OCC(D, DROP))))
 void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BM = BWD_DKDV_BM;       // query rows per step
   constexpr int BN = BWD_DKDV_BN;       // keys per workgroup (32 per wave)

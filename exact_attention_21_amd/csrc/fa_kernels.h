@@ -83,6 +83,13 @@ constexpr int BWD_DKDV_BM = 32;
 #ifndef BWD_DKDV_WAVES_PER_SIMD
 #define BWD_DKDV_WAVES_PER_SIMD 2
 #endif
+// d = 64 fits more waves per SIMD
+#ifndef BWD_DQ_WAVES_D64
+#define BWD_DQ_WAVES_D64 4
+#endif
+#ifndef BWD_DKDV_WAVES_D64
+#define BWD_DKDV_WAVES_D64 3
+#endif
 // Ring slots of the dK/dV pass: Q/dO tiles are loaded NSLOT - 1 steps ahead.
 #ifndef BWD_DKDV_NSLOT
 #define BWD_DKDV_NSLOT 2
