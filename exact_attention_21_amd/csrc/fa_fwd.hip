@@ -22,11 +22,19 @@
 // folded into the score scale.
 //
 // K/V tiles reach LDS by direct buffer->LDS loads (no staging registers) one
-// step ahead, into rings of two slots.  Tiles are stored with unpadded rows and
-// an XOR swizzle of the 16-byte chunk index chosen per access pattern (K: chunk
-// ^ (row & 15), conflict-free for the 16-byte fragment reads; V: chunk ^ ((row
-// & 3) << 1), conflict-free for the transposing reads).  Rows past the end of
-// the sequence load as zeros (hardware range check).
+// step ahead, into rings of two slots (one LDS object per slot, so that the
+// compiler sees the load into one slot and the reads of the other do not
+// alias).  Tiles are stored with unpadded rows and an XOR swizzle of the
+// 16-byte chunk index chosen per access pattern (K: chunk ^ (row & 15) at
+// d = 128, conflict-free for the 16-byte fragment reads; V: a swizzle of row
+// bits 0..3 conflict-free for the transposing reads).  Rows past the valid
+// length load as zeros (hardware range check of the buffer resource).
+//
+// One kernel serves the square, padded / cross-attention, dropout and
+// split-over-keys entry points: per batch entry it reads the valid lengths Lq,
+// Lk and shifts the causal limit by Lk - Lq; DROP adds the Philox keep bits to
+// P; SPLIT restricts the workgroup to one chunk of keys and writes fp32
+// partials for the merge kernel below.
 //
 // Latency is hidden by occupancy rather than by software pipelining: the kernel
 // fits in 168 VGPRs, so three workgroups (12 waves) share a CU and the
