@@ -111,6 +111,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                            0x00020000);
 }
 
+// A wave-uniform pointer moved to scalar registers (so that a buffer resource
+// built from it needs no per-lane handling).
+__device__ __forceinline__ const char *uniform_ptr(const char *ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }

@@ -151,10 +151,8 @@ void fwd_kernel(FwdParams p) {
   seq_lengths(p.seq, bh / p.seq.H, Lq, Lk);
   const int shift = Lk - Lq;
   const size_t qoff = (size_t)bh * (size_t)Nq * D, koff = (size_t)bh * (size_t)Nk * D;
-  // resources end at the valid rows: padding queries and keys read as zeros
+  // resources end at the valid rows: padding queries (and keys, below) read as zeros
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + qoff, (uint32_t)Lq * RB);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + koff, (uint32_t)Lk * RB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + koff, (uint32_t)Lk * RB);
   const int wr0 = i0 + w * WR;  // first query row of this wave
 
   // keys the workgroup's rows can see (none if all its rows are padding)
@@ -174,13 +172,21 @@ void fwd_kernel(FwdParams p) {
     dma_k_off[j] = (uint32_t)(row * RB + ((pos ^ swz_k<D>(row)) << 4));
     dma_v_off[j] = (uint32_t)(row * RB + ((pos ^ swz_v<D>(row)) << 4));
   }
-  auto issue_tile = [&](const __amdgpu_buffer_rsrc_t &rsrc, int t, char *slot,
-                        const uint32_t (&offs)[BPW]) {
-    // tiles outside [0, nt) load as zeros (offset past the resource end)
+  // Each tile gets a buffer resource of its own (scalar arithmetic), so the
+  // per-lane offsets stay loop-invariant: the resource starts at the tile and
+  // ends at the valid keys; tiles outside [t_beg, t_end) get zero records and
+  // load as zeros.
+  const char *k_head = reinterpret_cast<const char *>(p.k) + koff * 2;
+  const char *v_head = reinterpret_cast<const char *>(p.v) + koff * 2;
+  const uint32_t kv_bytes = (uint32_t)Lk * RB;
+  auto issue_tile = [&](const char *head, int t, char *slot, const uint32_t (&offs)[BPW]) {
     const bool ok = t >= t_beg && t < t_end;
-    const uint32_t base = ok ? (uint32_t)t * TB : 0x80000000u;
+    // the values are wave-uniform; readfirstlane keeps them (and the resource) in SGPRs
+    const uint32_t tb = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)t * TB : 0u);
+    const uint32_t n = __builtin_amdgcn_readfirstlane(ok && tb < kv_bytes ? kv_bytes - tb : 0u);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(head + tb), n);
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) dma16(rsrc, slot + (w * BPW + j) * 1024, base + offs[j]);
+    for (int j = 0; j < BPW; ++j) dma16(r, slot + (w * BPW + j) * 1024, offs[j]);
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
@@ -332,8 +338,8 @@ void fwd_kernel(FwdParams p) {
   // K(t) and V(t) go to ring slot SL
   auto issue_step = [&](int t, auto slot) {
     constexpr int SL = decltype(slot)::value;
-    issue_tile(rk, t, SL == 0 ? k_slot0 : k_slot1, dma_k_off);
-    issue_tile(rv, t, SL == 0 ? v_slot0 : v_slot1, dma_v_off);
+    issue_tile(k_head, t, SL == 0 ? k_slot0 : k_slot1, dma_k_off);
+    issue_tile(v_head, t, SL == 0 ? v_slot0 : v_slot1, dma_v_off);
   };
   // one step on tile t held in slot SL; tile t + 1 is loaded into the other slot
   auto step = [&](int t, auto slot) {
