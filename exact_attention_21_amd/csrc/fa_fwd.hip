@@ -44,7 +44,11 @@
 // rescale is a wave-uniform, rarely taken branch).  Between raises the
 // exponentials are taken against a stale max, so p <= 2^8; the final
 // normalisation uses the same stale max in numerator and denominator, so the
-// result is unchanged.
+// result is unchanged.  A tile's row max is only needed when some p would
+// exceed 2^8, so each tile first takes the exponentials against the running
+// max and checks every lane's partial row sum against 2^8; only a wave in
+// which a sum exceeds it (a row's first visible tile always does) computes the
+// row max, updates and takes the exponentials again.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -55,6 +59,7 @@ namespace fa {
 namespace {
 
 constexpr float LAZY_TAU = 8.0f;  // log2 growth of a row max that forces a rescale
+constexpr float LAZY_BOUND = 256.0f;  // 2^LAZY_TAU: largest probability kept without a rescale
 constexpr float M_FLOOR = -1e30f; // initial running max (log2 units)
 constexpr int NSLOT = 2;          // ring slots per K and V (tiles are loaded one step ahead)
 
@@ -267,10 +272,48 @@ void fwd_kernel(FwdParams p) {
       }
     }
   };
-  // softmax of one tile: new (lazy) running max, probabilities packed to 16 bits,
-  // row sums; returns whether the running max moved (output must be rescaled)
+  // probabilities p = exp2(s * scale * log2(e) - m) of one block against the
+  // reference max m, packed to 16 bits (dropout-masked), and this lane's share
+  // of the row sum, taken from the unrounded, unmasked values
+  auto probs = [&](const f32x16 &s, float m, uint32_t (&pk)[8], uint32_t keep) {
+    const float nm = -m;
+    float ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e0 = fast_exp2(__builtin_fmaf(s[2 * j], sl2, nm));
+      const float e1 = fast_exp2(__builtin_fmaf(s[2 * j + 1], sl2, nm));
+      if constexpr (DROP)  // dropped weights leave P V but not the row sum
+        pk[j] = T::pack((keep >> (2 * j)) & 1 ? e0 : 0.f, (keep >> (2 * j + 1)) & 1 ? e1 : 0.f);
+      else
+        pk[j] = T::pack(e0, e1);
+      ls = j == 0 ? e0 + e1 : ls + (e0 + e1);
+    }
+    return ls;
+  };
+  // softmax of one tile; returns whether a running max moved (the output must
+  // be rescaled).  Fast path: the probabilities against the current running
+  // max are final when none exceeds 2^tau, which a lane's partial row sum
+  // <= 2^tau guarantees (the sum is +inf on a row's first visible tile, whose
+  // running max is still the floor, and NaN fails the test too).  Otherwise,
+  // for the whole wave: the lazy update of the running max from the tile's row
+  // max, and the probabilities again.
   auto stage_softmax = [&](f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&alpha)[QB],
                            const uint32_t (&keep)[QB]) {
+    float ls[QB];
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      ls[qb] = probs(s[qb], mrun[qb], pk[qb], keep[qb]);
+      over |= !(ls[qb] <= LAZY_BOUND);
+    }
+    if (__builtin_amdgcn_ballot_w64(over) == 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        alpha[qb] = 1.f;
+        lrun[qb] += ls[qb];
+      }
+      return false;
+    }
     bool grow_any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -284,19 +327,7 @@ void fwd_kernel(FwdParams p) {
       alpha[qb] = grow ? fast_exp2(mrun[qb] - mx) : 1.f;
       grow_any |= grow;
       mrun[qb] = mu;
-      const float nm = -mu;
-      float ls = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float e0 = fast_exp2(__builtin_fmaf(s[qb][2 * j], sl2, nm));
-        const float e1 = fast_exp2(__builtin_fmaf(s[qb][2 * j + 1], sl2, nm));
-        if constexpr (DROP)  // dropped weights leave P V but not the row sum
-          pk[qb][j] = T::pack((keep[qb] >> (2 * j)) & 1 ? e0 : 0.f, (keep[qb] >> (2 * j + 1)) & 1 ? e1 : 0.f);
-        else
-          pk[qb][j] = T::pack(e0, e1);
-        ls += e0 + e1;  // row sum from the unrounded probabilities (LSE accuracy)
-      }
-      lrun[qb] = lrun[qb] * alpha[qb] + ls;
+      lrun[qb] = lrun[qb] * alpha[qb] + probs(s[qb], mu, pk[qb], keep[qb]);
     }
     return grow_any;
   };
