@@ -8,7 +8,7 @@
 //   dS = P (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
 // Three kernels, none with atomics (so every output is bitwise reproducible):
-//   bwd_pre_kernel   D = rowsum(dO * O) and LSE * log2(e), fp32 [B][H][Nq]
+//   bwd_pre_kernel   -D = -rowsum(dO * O) and LSE * log2(e), fp32 [B][H][Nq]
 //   bwd_dq_kernel    one workgroup per 128 query rows, K/V tiles streamed through
 //                    LDS (the forward's structure): S^T = K Q^T, dP^T = V dO^T,
 //                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
   if (row < rows && sub == 0) {
-    dws[row] = acc;
+    dws[row] = -acc;  // -D: the passes start their dP accumulation from it
     const float l = lse[row];  // -inf: the row sees no key; +inf makes its P = 0
     lse2[row] = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
   }
@@ -164,7 +164,14 @@ void bwd_dq_kernel(BwdParams p) {
 
   // per-lane row statistics; padding rows get lse2 = +inf so that P = 0
   const float lse2 = qrow < Lq ? p.lse2[(size_t)bh * Nq + qrow] : __builtin_inff();
-  const float dsum = qrow < Lq ? p.dws[(size_t)bh * Nq + qrow] : 0.f;
+  const float ndsum = qrow < Lq ? p.dws[(size_t)bh * Nq + qrow] : 0.f;  // -D
+  // dP^T accumulates from -D (16 loop-invariant registers), so the MFMAs give
+  // dP^T - D; with dropout dP is scaled first, and at d = 64 the registers are
+  // not there (occupancy 4): both start from 0 and subtract
+  constexpr bool DP_FROM_D = !DROP && D == 128;
+  f32x16 dp_init;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dp_init[r] = DP_FROM_D ? ndsum : 0.f;
 
   // Q and dO fragments: B operands of S^T = K Q^T and dP^T = V dO^T
   u32x4 qf[ND16], dof[ND16];
@@ -227,13 +234,14 @@ void bwd_dq_kernel(BwdParams p) {
     const char *vs = SL == 0 ? v_slot0 : v_slot1;
     asm volatile("" : "+v"(kf_base), "+v"(vf_base), "+v"(t_base[0]), "+v"(t_base[1]));
     // S^T = K Q^T and dP^T = V dO^T (keys x queries)
-    f32x16 s = f32x16{}, dp = f32x16{};
+    f32x16 s = f32x16{}, dp = dp_init;
 #pragma unroll
     for (int db = 0; db < ND16; ++db) {
       s = T::mma(lds_read16(ks + (kf_base ^ (uint32_t)(32 * db))), qf[db], s);
       dp = T::mma(lds_read16(vs + (vf_base ^ (uint32_t)(32 * db))), dof[db], dp);
     }
-    // P^T = exp2(scale log2e S - LSE log2e), masked; dS^T = P^T (dP^T - D)
+    // P^T = exp2(scale log2e S - LSE log2e), masked; dS^T = P^T (dP^T - D),
+    // the difference already formed by the MFMAs
     const int j0 = t * BN;
     const bool need_mask = (CAUSAL && j0 + BN - 1 > wr0 + shift) || (j0 + BN > Lk);
     // dropout: dP is masked and scaled (dS = P (Z dP - D), Z = keep * 256 / (256 - p8))
@@ -256,9 +264,11 @@ void bwd_dq_kernel(BwdParams p) {
         const int r = 2 * j + e;
         const float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lse2));  // masked: exp2(-inf) = 0
         if constexpr (DROP)
-          v2[e] = pr * (((keep >> r) & 1 ? dp[r] * p.drop.scale : 0.f) - dsum);
+          v2[e] = pr * ((keep >> r) & 1 ? __builtin_fmaf(dp[r], p.drop.scale, ndsum) : ndsum);
+        else if constexpr (DP_FROM_D)
+          v2[e] = pr * dp[r];
         else
-          v2[e] = pr * (dp[r] - dsum);
+          v2[e] = pr * (dp[r] + ndsum);
       }
       dsk[j] = T::pack(v2[0], v2[1]);
     }
@@ -322,7 +332,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NS = BWD_DKDV_NSLOT;    // ring slots (loads run NS - 1 steps ahead)
   constexpr int RB = D * 2;
   constexpr int TB = BM * RB;           // bytes per Q (or dO) tile
-  constexpr int STAT = BWD_DKDV_STAT;   // LSE2 (64 floats read, 32 used), then D
+  constexpr int STAT = BWD_DKDV_STAT;   // LSE2 (64 floats read, 32 used), then -D
   constexpr int SLOT = 2 * TB + STAT;   // Q, dO, stats
   constexpr int CPR = RB / 16;
   constexpr int ROWS_PER_BLOCK = 64 / CPR;
@@ -461,13 +471,21 @@ void bwd_dkdv_kernel(BwdParams p) {
     issue_step(i + NS - 1, std::integral_constant<int, (SL + NS - 1) % NS>{});
     const char *qs = slot_base(slot);
     const char *ds = qs + TB;
-    const float *ls = reinterpret_cast<const float *>(qs + 2 * TB);  // LSE2 at [0, 32), D at [64, 96)
+    const float *ls = reinterpret_cast<const float *>(qs + 2 * TB);  // LSE2 at [0, 32), -D at [64, 96)
     const int q0 = (qt0 + i) * BM;
     // keep the per-block addresses out of the loop-invariant set: they are two
     // cheap VALU ops each, registers are not
     asm volatile("" : "+v"(f_base), "+v"(t_base[0]), "+v"(t_base[1]));
-    // S = Q K^T and dP = dO V^T (queries x keys): lane = key, registers = queries
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // S = Q K^T and dP = dO V^T (queries x keys): lane = key, registers = queries.
+    // dP accumulates from -D of each register's query row (the stats slot holds
+    // -D at [64, 96)), so the MFMAs give dP - D; with dropout dP starts from 0
+    f32x16 s = f32x16{}, dp;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4 nd = DROP ? f32x4{} : *reinterpret_cast<const f32x4 *>(ls + 64 + 8 * rg + 4 * hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * rg + e] = nd[e];
+    }
 #pragma unroll
     for (int db = 0; db < ND16; ++db) {
       const uint32_t fa = f_base ^ (uint32_t)(32 * db);
@@ -491,7 +509,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int rg = 0; rg < 4; ++rg) {
       const int qr = 8 * rg + 4 * hi;  // 4 consecutive query rows of this register group
       const f32x4 lq = *reinterpret_cast<const f32x4 *>(ls + qr);
-      const f32x4 dq = *reinterpret_cast<const f32x4 *>(ls + 64 + qr);
+      const f32x4 nd = DROP ? *reinterpret_cast<const f32x4 *>(ls + 64 + qr) : f32x4{};  // -D
       float pv[4], sv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -501,10 +519,10 @@ void bwd_dkdv_kernel(BwdParams p) {
         if constexpr (DROP) {
           const bool kept = (keep >> r) & 1;
           pv[e] = kept ? pr : 0.f;
-          sv[e] = pr * ((kept ? dp[r] * p.drop.scale : 0.f) - dq[e]);
+          sv[e] = pr * (kept ? __builtin_fmaf(dp[r], p.drop.scale, nd[e]) : nd[e]);
         } else {
           pv[e] = pr;
-          sv[e] = pr * (dp[r] - dq[e]);
+          sv[e] = pr * dp[r];  // dp already holds dP - D
         }
       }
       pk[2 * rg] = T::pack(pv[0], pv[1]);

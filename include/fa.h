@@ -73,7 +73,7 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            void *stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: D = rowsum(dO * O) and LSE * log2(e),
+ * Bytes of device workspace fa_bwd needs: -D = -rowsum(dO * O) and LSE * log2(e),
  * each fp32 [B][H][N] and 256-byte aligned.  Returns 0 for invalid shapes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
@@ -103,7 +103,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
  *   fa_bwd_preprocess -> fa_bwd_dkdv -> fa_bwd_dq
  * (the last two only read the workspace and may run in either order).
  *
- * fa_bwd_preprocess: reads o, dout and lse; writes D_i = sum_c dO_ic O_ic and
+ * fa_bwd_preprocess: reads o, dout and lse; writes -D_i = -sum_c dO_ic O_ic and
  *   lse * log2(e) (fp32) into the workspace.
  * fa_bwd_dkdv: recomputes P and dS key-block by key-block; writes dk and dv.
  * fa_bwd_dq: recomputes P and dS query-block by query-block; writes dq.
