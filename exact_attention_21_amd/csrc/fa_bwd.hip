@@ -232,7 +232,6 @@ void bwd_dq_kernel(BwdParams p) {
     issue_step(t + 1, std::integral_constant<int, SL ^ 1>{});
     const char *ks = SL == 0 ? k_slot0 : k_slot1;
     const char *vs = SL == 0 ? v_slot0 : v_slot1;
-    asm volatile("" : "+v"(kf_base), "+v"(vf_base), "+v"(t_base[0]), "+v"(t_base[1]));
     // S^T = K Q^T and dP^T = V dO^T (keys x queries)
     f32x16 s = f32x16{}, dp = dp_init;
 #pragma unroll
