@@ -131,6 +131,28 @@ def test_large_scores_stay_finite(gpu):
     check_full(q, k, vb, "f16", False, gpu)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rising_scores_exercise_every_softmax_path(gpu, d, causal, dtype):
+    # Scores rise with the key index in steps, so successive 32-key tiles raise a
+    # row's max by about 5, then by about 20 (log2 units), then by 5 again: the
+    # kernel's tile row sums exceed 2^8 both with a max that moved less than
+    # 2^8 (probabilities kept) and with one that moved more (running max, row
+    # sum and output rescaled).  q_i = ones + noise, k_j = c_j * ones + noise.
+    B, H, N = 1, 2, 320
+    rng = np.random.default_rng(83 + d)
+    step = np.array([0.0, 5.0, 25.0, 30.0, 50.0, 55.0, 75.0, 80.0, 100.0, 105.0]) / 1.4426950408889634
+    scale = 1 / math.sqrt(d)
+    c = np.repeat(step, 32)[:N] / (scale * d)  # key j's score ~ step of its tile (natural log units)
+    q = np.ones((B, H, N, d)) + 0.05 * rng.standard_normal((B, H, N, d))
+    k = c[None, None, :, None] * np.ones((B, H, N, d)) + 0.05 * rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    qb, kb, vb = (fa_inputs.narrow(x, dtype) for x in (q, k, v))
+    say(f"[fwd rising scores] d={d} causal={causal} {dtype}")
+    check_full(qb, kb, vb, dtype, causal, gpu)
+
+
 def test_forward_is_bitwise_repeatable(gpu):
     qb, kb, vb = fa_inputs.qkv_bits(2, 8, 2048, 128, "bf16", seed=82)
     o1, l1 = run_fwd(qb, kb, vb, "bf16", True, gpu)
