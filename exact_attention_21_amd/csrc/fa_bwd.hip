@@ -244,9 +244,8 @@ void bwd_dq_kernel(BwdParams p) {
     const int j0 = t * BN;
     const bool need_mask = (CAUSAL && j0 + BN - 1 > wr0 + shift) || (j0 + BN > Lk);
     // dropout: dP is masked and scaled (dS = P (Z dP - D), Z = keep * 256 / (256 - p8))
-    const uint32_t keep = DROP ? keep_bits_query_major(qrow, j0, hi, (uint32_t)bh, p.drop.offset,
-                                                       p.drop.k0, p.drop.k1, p.drop.p8)
-                               : 0u;
+    const u32x4 keep = DROP ? keep_bytes_query_major(qrow, j0, hi, (uint32_t)bh, p.drop.offset, p.drop.k0, p.drop.k1)
+                            : u32x4{};
     if (need_mask) {  // a separate block: most steps skip it
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -263,7 +262,7 @@ void bwd_dq_kernel(BwdParams p) {
         const int r = 2 * j + e;
         const float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lse2));  // masked: exp2(-inf) = 0
         if constexpr (DROP)
-          v2[e] = pr * ((keep >> r) & 1 ? __builtin_fmaf(dp[r], p.drop.scale, ndsum) : ndsum);
+          v2[e] = pr * (kept(keep, r, p.drop.p8) ? __builtin_fmaf(dp[r], p.drop.scale, ndsum) : ndsum);
         else if constexpr (DP_FROM_D)
           v2[e] = pr * dp[r];
         else
@@ -493,9 +492,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
     const bool need_mask = CAUSAL && q0 + shift < kw0 + 31;
     // dropout: dV takes P * keep (scaled in the epilogue), dS = P (Z dP - D)
-    const uint32_t keep = DROP ? keep_bits_key_major(key, q0, hi, (uint32_t)bh, p.drop.offset,
-                                                     p.drop.k0, p.drop.k1, p.drop.p8)
-                               : 0u;
+    const u32x4 keep = DROP ? keep_bytes_key_major(key, q0, hi, (uint32_t)bh, p.drop.offset, p.drop.k0, p.drop.k1)
+                            : u32x4{};
     if (need_mask) {  // a separate block: most steps skip it
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -516,9 +514,9 @@ void bwd_dkdv_kernel(BwdParams p) {
         // rows past Lq load LSE2 = D = 0 and Q = dO = 0, so they contribute nothing
         const float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lq[e]));  // masked: exp2(-inf) = 0
         if constexpr (DROP) {
-          const bool kept = (keep >> r) & 1;
-          pv[e] = kept ? pr : 0.f;
-          sv[e] = pr * (kept ? __builtin_fmaf(dp[r], p.drop.scale, nd[e]) : nd[e]);
+          const bool kp = kept(keep, r, p.drop.p8);
+          pv[e] = kp ? pr : 0.f;
+          sv[e] = pr * (kp ? __builtin_fmaf(dp[r], p.drop.scale, nd[e]) : nd[e]);
         } else {
           pv[e] = pr;
           sv[e] = pr * dp[r];  // dp already holds dP - D

@@ -167,8 +167,10 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    // 64-bit products: one v_mad_u64_u32 each instead of a mul_lo / mul_hi pair
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0], p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     c = u32x4{hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0};
   }
   return c;
@@ -200,41 +202,32 @@ __device__ __forceinline__ u32x4 byte_transpose(u32x4 x) {
                __builtin_amdgcn_perm(hi23, hi01, 0x05040100u), __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
 }
 
-// Keep bits of the 16 (query, key) pairs an MFMA accumulator lane holds, bit r
-// for register r = 4a + b.  A pair (i, j) of head bh is kept iff byte j % 4 of
-// word i % 4 of Philox(counter = (j / 4, i / 4, bh, offset), key) >= p8.
+// Dropout bytes of the 16 (query, key) pairs an MFMA accumulator lane holds:
+// byte b of word a belongs to register r = 4a + b.  A pair (i, j) of head bh is
+// kept iff byte j % 4 of word i % 4 of Philox(counter = (j / 4, i / 4, bh,
+// offset), key) >= p8 (see kept()).
 // Query-major lanes (one query i, keys j0 + 8a + 4hi + b): the lane computes the
 // block of key group j0/4 + 2t + hi (t = i % 4, quad member), and the quad
 // transpose hands every lane word i % 4 of the four blocks it needs.
-__device__ __forceinline__ uint32_t keep_bits_query_major(int i, int j0, int hi, uint32_t bh,
-                                                          uint32_t offset, uint32_t k0,
-                                                          uint32_t k1, uint32_t p8) {
+__device__ __forceinline__ u32x4 keep_bytes_query_major(int i, int j0, int hi, uint32_t bh,
+                                                        uint32_t offset, uint32_t k0, uint32_t k1) {
   const int t = i & 3;
   const u32x4 r = philox4x32_10(u32x4{(uint32_t)(j0 / 4 + 2 * t + hi), (uint32_t)(i / 4), bh, offset}, k0, k1);
-  const u32x4 w = quad_transpose(r);
-  uint32_t bits = 0;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) bits |= (uint32_t)(((w[a] >> (8 * b)) & 0xFFu) >= p8) << (4 * a + b);
-  return bits;
+  return quad_transpose(r);
 }
 // Key-major lanes (one key j, queries i0 + 8a + 4hi + b): the lane computes the
 // block of query group i0/4 + 2t + hi (t = j % 4), gathers byte t' of its four
 // words for each quad member t', and the quad transpose hands lane t the bytes
 // of key offset t for the four query groups.
-__device__ __forceinline__ uint32_t keep_bits_key_major(int j, int i0, int hi, uint32_t bh,
-                                                        uint32_t offset, uint32_t k0,
-                                                        uint32_t k1, uint32_t p8) {
+__device__ __forceinline__ u32x4 keep_bytes_key_major(int j, int i0, int hi, uint32_t bh,
+                                                      uint32_t offset, uint32_t k0, uint32_t k1) {
   const int t = j & 3;
   const u32x4 r = philox4x32_10(u32x4{(uint32_t)(j / 4), (uint32_t)(i0 / 4 + 2 * t + hi), bh, offset}, k0, k1);
-  const u32x4 w = quad_transpose(byte_transpose(r));
-  uint32_t bits = 0;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) bits |= (uint32_t)(((w[a] >> (8 * b)) & 0xFFu) >= p8) << (4 * a + b);
-  return bits;
+  return quad_transpose(byte_transpose(r));
+}
+// Whether register r's pair is kept (a byte compare, SDWA on gfx950).
+__device__ __forceinline__ bool kept(const u32x4 &w, int r, uint32_t p8) {
+  return ((w[r >> 2] >> (8 * (r & 3))) & 0xFFu) >= p8;
 }
 
 }  // namespace fa

@@ -275,7 +275,7 @@ void fwd_kernel(FwdParams p) {
   // probabilities p = exp2(s * scale * log2(e) - m) of one block against the
   // reference max m, packed to 16 bits (dropout-masked), and this lane's share
   // of the row sum, taken from the unrounded, unmasked values
-  auto probs = [&](const f32x16 &s, float m, uint32_t (&pk)[8], uint32_t keep) {
+  auto probs = [&](const f32x16 &s, float m, uint32_t (&pk)[8], const u32x4 &keep) {
     const float nm = -m;
     float ls = 0.f;
 #pragma unroll
@@ -283,7 +283,7 @@ void fwd_kernel(FwdParams p) {
       const float e0 = fast_exp2(__builtin_fmaf(s[2 * j], sl2, nm));
       const float e1 = fast_exp2(__builtin_fmaf(s[2 * j + 1], sl2, nm));
       if constexpr (DROP)  // dropped weights leave P V but not the row sum
-        pk[j] = T::pack((keep >> (2 * j)) & 1 ? e0 : 0.f, (keep >> (2 * j + 1)) & 1 ? e1 : 0.f);
+        pk[j] = T::pack(kept(keep, 2 * j, p.drop.p8) ? e0 : 0.f, kept(keep, 2 * j + 1, p.drop.p8) ? e1 : 0.f);
       else
         pk[j] = T::pack(e0, e1);
       ls = j == 0 ? e0 + e1 : ls + (e0 + e1);
@@ -298,7 +298,7 @@ void fwd_kernel(FwdParams p) {
   // for the whole wave: the lazy update of the running max from the tile's row
   // max, and the probabilities again.
   auto stage_softmax = [&](f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&alpha)[QB],
-                           const uint32_t (&keep)[QB]) {
+                           const u32x4 (&keep)[QB]) {
     float ls[QB];
     bool over = false;
 #pragma unroll
@@ -376,12 +376,12 @@ void fwd_kernel(FwdParams p) {
   auto step = [&](int t, auto slot) {
     constexpr int SL = decltype(slot)::value;
     issue_step(t + 1, std::integral_constant<int, SL ^ 1>{});
-    uint32_t keep[QB] = {};
-    if constexpr (DROP) {  // dropout keep bits of this lane's 16 pairs per query block
+    u32x4 keep[QB] = {};
+    if constexpr (DROP) {  // dropout bytes of this lane's 16 pairs per query block
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        keep[qb] = keep_bits_query_major(wr0 + qb * 32 + l32, t * BN, hi, (uint32_t)bh, p.drop.offset,
-                                         p.drop.k0, p.drop.k1, p.drop.p8);
+        keep[qb] = keep_bytes_query_major(wr0 + qb * 32 + l32, t * BN, hi, (uint32_t)bh, p.drop.offset,
+                                          p.drop.k0, p.drop.k1);
     }
     stage_s(slot, sacc);
     if (needs_mask(t)) apply_mask(t, sacc);
