@@ -97,10 +97,8 @@ static_assert(swz_v_period16<64>() && swz_v_period16<128>(), "V swizzle must rep
 
 }  // namespace
 
-// waves per SIMD: two query blocks per wave, or dropout's generator state at
-// d = 128, need the registers of occupancy 2
-#define FWD_OCC(D, QB, DROP) \
-  ((QB) == 2 || ((DROP) && (D) == 128) ? 2 : (D) == 64 ? FWD_WAVES_D64 : FWD_WAVES_PER_SIMD)
+// waves per SIMD: two query blocks per wave need the registers of occupancy 2
+#define FWD_OCC(D, QB, DROP) ((QB) == 2 ? 2 : (D) == 64 ? FWD_WAVES_D64 : FWD_WAVES_PER_SIMD)
 
 template <class T, int D, int QB, bool CAUSAL, bool O_IN_AGPR, bool DROP, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FWD_OCC(D, QB, DROP), FWD_OCC(D, QB, DROP))))
@@ -376,14 +374,16 @@ void fwd_kernel(FwdParams p) {
   auto step = [&](int t, auto slot) {
     constexpr int SL = decltype(slot)::value;
     issue_step(t + 1, std::integral_constant<int, SL ^ 1>{});
+    stage_s(slot, sacc);
+    // dropout bytes of this lane's 16 pairs per query block (generated after
+    // the S MFMAs are issued: fewer registers live across them)
     u32x4 keep[QB] = {};
-    if constexpr (DROP) {  // dropout bytes of this lane's 16 pairs per query block
+    if constexpr (DROP) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         keep[qb] = keep_bytes_query_major(wr0 + qb * 32 + l32, t * BN, hi, (uint32_t)bh, p.drop.offset,
                                           p.drop.k0, p.drop.k1);
     }
-    stage_s(slot, sacc);
     if (needs_mask(t)) apply_mask(t, sacc);
     float alpha[QB];
     const bool resc = stage_softmax(sacc, pk, alpha, keep);
