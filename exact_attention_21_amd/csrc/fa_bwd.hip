@@ -501,44 +501,48 @@ void bwd_dkdv_kernel(BwdParams p) {
         s[r] = key <= qrow + shift ? s[r] : -__builtin_inff();
       }
     }
-    uint32_t pk[8], sk[8];
+    // in two halves of 16 query rows (register groups 2kb, 2kb + 1): P and dS
+    // packed to 16 bits, then dV^T += dO^T P and dK^T += Q^T dS for that half
+    // (A operands by transposing reads); each accumulator still adds its kb = 0
+    // product before its kb = 1 product
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int qr = 8 * rg + 4 * hi;  // 4 consecutive query rows of this register group
-      const f32x4 lq = *reinterpret_cast<const f32x4 *>(ls + qr);
-      const f32x4 nd = DROP ? *reinterpret_cast<const f32x4 *>(ls + 64 + qr) : f32x4{};  // -D
-      float pv[4], sv[4];
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t pk[4], sk[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * rg + e;
-        // rows past Lq load LSE2 = D = 0 and Q = dO = 0, so they contribute nothing
-        const float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lq[e]));  // masked: exp2(-inf) = 0
-        if constexpr (DROP) {
-          const bool kp = kept(keep, r, p.drop.p8);
-          pv[e] = kp ? pr : 0.f;
-          sv[e] = pr * (kp ? __builtin_fmaf(dp[r], p.drop.scale, nd[e]) : nd[e]);
-        } else {
-          pv[e] = pr;
-          sv[e] = pr * dp[r];  // dp already holds dP - D
+      for (int h = 0; h < 2; ++h) {
+        const int rg = 2 * kb + h;
+        const int qr = 8 * rg + 4 * hi;  // 4 consecutive query rows of this register group
+        const f32x4 lq = *reinterpret_cast<const f32x4 *>(ls + qr);
+        const f32x4 nd = DROP ? *reinterpret_cast<const f32x4 *>(ls + 64 + qr) : f32x4{};  // -D
+        float pv[4], sv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rg + e;
+          // rows past Lq load LSE2 = D = 0 and Q = dO = 0, so they contribute nothing
+          const float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lq[e]));  // masked: exp2(-inf) = 0
+          if constexpr (DROP) {
+            const bool kp = kept(keep, r, p.drop.p8);
+            pv[e] = kp ? pr : 0.f;
+            sv[e] = pr * (kp ? __builtin_fmaf(dp[r], p.drop.scale, nd[e]) : nd[e]);
+          } else {
+            pv[e] = pr;
+            sv[e] = pr * dp[r];  // dp already holds dP - D
+          }
         }
+        pk[2 * h] = T::pack(pv[0], pv[1]);
+        pk[2 * h + 1] = T::pack(pv[2], pv[3]);
+        sk[2 * h] = T::pack(sv[0], sv[1]);
+        sk[2 * h + 1] = T::pack(sv[2], sv[3]);
       }
-      pk[2 * rg] = T::pack(pv[0], pv[1]);
-      pk[2 * rg + 1] = T::pack(pv[2], pv[3]);
-      sk[2 * rg] = T::pack(sv[0], sv[1]);
-      sk[2 * rg + 1] = T::pack(sv[2], sv[3]);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing reads)
+      const u32x4 bp = {pk[0], pk[1], pk[2], pk[3]};
+      const u32x4 bs = {sk[0], sk[1], sk[2], sk[3]};
 #pragma unroll
-    for (int c = 0; c < ND32; ++c) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int c = 0; c < ND32; ++c) {
         const uint32_t ta0 = t_base[0] ^ (uint32_t)(64 * c), ta1 = t_base[1] ^ (uint32_t)(64 * c);
         const u32x2 d0 = lds_read_tr4(ds + kb * 16 * RB + ta0);
         const u32x2 d1 = lds_read_tr4(ds + kb * 16 * RB + ta1);
         const u32x2 q0v = lds_read_tr4(qs + kb * 16 * RB + ta0);
         const u32x2 q1v = lds_read_tr4(qs + kb * 16 * RB + ta1);
-        const u32x4 bp = {pk[4 * kb], pk[4 * kb + 1], pk[4 * kb + 2], pk[4 * kb + 3]};
-        const u32x4 bs = {sk[4 * kb], sk[4 * kb + 1], sk[4 * kb + 2], sk[4 * kb + 3]};
         dvacc[c] = T::mma(u32x4{d0[0], d0[1], d1[0], d1[1]}, bp, dvacc[c]);
         dkacc[c] = T::mma(u32x4{q0v[0], q0v[1], q1v[0], q1v[1]}, bs, dkacc[c]);
       }
