@@ -78,24 +78,36 @@ int fwd_qb(int N, int d) { return d == 128 ? FWD_QB_D128 : (N > 128 ? FWD_QB_D64
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Key chunks of the split forward: about 4096 workgroups (the GPU holds 768 at
-// once, so the last partial round of workgroups costs little), at least 256
-// keys per chunk, chunk a multiple of two key tiles.
+// Key chunks of the split forward.  Its workgroups all carry about the same
+// work, and the GPU holds 768 of them at once (256 CUs x 3), so the chunk count
+// is chosen by how well the grid fills whole rounds of 768: the smallest count
+// whose rounds are >= 95 % full (else the fullest), with at least 256 keys
+// per chunk and chunks a multiple of two key tiles.
 struct SplitPlan {
   int bm, n_qtiles, nsplit, chunk;
 };
 SplitPlan split_plan(int B, int H, int Nq, int Nk, int d) {
+  constexpr long long kResident = 256 * 3;
   SplitPlan sp;
   sp.bm = 128 * (d == 128 ? FWD_QB_D128 : 1);
   sp.n_qtiles = (Nq + sp.bm - 1) / sp.bm;
   const long long units = (long long)B * H * sp.n_qtiles;
-  long long want = (4096 + units - 1) / units;
   const long long most = ((long long)Nk + 255) / 256;
-  if (want > most) want = most;
-  if (want < 1) want = 1;
   const long long tiles2 = 2LL * fa::FWD_BN;
-  sp.chunk = (int)((((long long)Nk + want - 1) / want + tiles2 - 1) / tiles2 * tiles2);
-  sp.nsplit = (int)(((long long)Nk + sp.chunk - 1) / sp.chunk);
+  double best_fill = -1.0;
+  for (long long want = 1; want <= most && want <= 4 * kResident; ++want) {
+    const long long chunk = ((long long)Nk + want - 1) / want;
+    const long long c = (chunk + tiles2 - 1) / tiles2 * tiles2;
+    const long long n = ((long long)Nk + c - 1) / c;
+    const long long wgs = units * n;
+    const double fill = (double)wgs / (double)(((wgs + kResident - 1) / kResident) * kResident);
+    if (fill > best_fill + 1e-9) {
+      best_fill = fill;
+      sp.chunk = (int)c;
+      sp.nsplit = (int)n;
+    }
+    if (fill >= 0.95) break;
+  }
   return sp;
 }
 
@@ -138,7 +150,7 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *pl
   plan->block_n = bn;
   plan->threads = 256;
   plan->grid = (int)grid;
-  plan->lds_bytes = 2 * 2 * bn * d * 2;  // K and V rings of two tiles
+  plan->lds_bytes = (d == 128 ? FWD_NSLOT_D128 : 2) * 2 * bn * d * 2;  // K and V rings (no dropout)
   plan->xcd_grouped = ((long long)B * H) % 8 == 0;
   return FA_OK;
 }

@@ -12,6 +12,12 @@ constexpr int FWD_BN = 32;
 // Query blocks of 32 rows per wave for head dim 128, and whether the output
 // accumulator is kept in AGPRs (set together with the compiler's MFMA register
 // form for fa_fwd.hip).
+#ifndef FWD_NSLOT_D128
+#define FWD_NSLOT_D128 3  // K/V ring slots of the d = 128 forward without dropout (tiles loaded NSLOT - 1 steps ahead)
+#endif
+#ifndef FWD_NSLOT_SPLIT
+#define FWD_NSLOT_SPLIT 3  // the same for the split forward (decode shapes)
+#endif
 #ifndef FWD_QB_D128
 #define FWD_QB_D128 1
 #endif
