@@ -97,6 +97,9 @@ constexpr int BWD_DKDV_BM = 32;
 #define BWD_DKDV_WAVES_D64 3
 #endif
 // Ring slots of the dK/dV pass: Q/dO tiles are loaded NSLOT - 1 steps ahead.
+#ifndef BWD_DQ_NSLOT_D128
+#define BWD_DQ_NSLOT_D128 3  // dQ pass K/V ring slots at d = 128 (loads run NSLOT - 1 steps ahead)
+#endif
 #ifndef BWD_DKDV_NSLOT
 #define BWD_DKDV_NSLOT 2
 #endif
