@@ -309,27 +309,26 @@ def main():
     scale = 1 / math.sqrt(d)
     stream = torch.cuda.current_stream()
 
-    # one step: forward, then the three backward stages; events bracket each
-    # kernel on the stream it runs on
+    # one step: forward, then the backward's two passes as fa_bwd runs them
+    # (the dQ pass also computes the row statistics the dK/dV pass reads);
+    # events bracket each kernel on the stream it runs on
     def step(ev=None):
         rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
         rec(0)
         fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
         rec(1)
         if not args.fwd_only:
-            fa.fa_bwd_preprocess(o, do, lse, ws, stream)
+            fa.fa_bwd_dq_preprocess(q, k, v, o, do, lse, dq, scale, causal, ws, stream)
             rec(2)
             fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, causal, ws, stream)
             rec(3)
-            fa.fa_bwd_dq(q, k, v, do, dq, scale, causal, ws, stream)
-            rec(4)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -348,11 +347,10 @@ def main():
         # algorithmic FLOP of each backward pass: dK/dV runs 4 of the tile
         # products (S, dP, dV, dK), dQ runs 3 (S, dP, dQ); each is 2 B H N^2 d
         # (halved when causal), i.e. half the nominal forward's 4 B H N^2 d
-        kern["bwd_pre_kernel"] = (avg_ms(1, 2), 0.0)
+        kern["bwd_dq_kernel"] = (avg_ms(1, 2), 1.5 * f_fwd)
         kern["bwd_dkdv_kernel"] = (avg_ms(2, 3), 2.0 * f_fwd)
-        kern["bwd_dq_kernel"] = (avg_ms(3, 4), 1.5 * f_fwd)
     fwd_avg = kern["fwd_kernel"][0]
-    bwd_avg = avg_ms(1, 4) if not args.fwd_only else 0.0
+    bwd_avg = avg_ms(1, 3) if not args.fwd_only else 0.0
     total_flop = f_fwd + (0 if args.fwd_only else f_bwd)
     fwd_tf = f_fwd / (fwd_avg * 1e-3) / 1e12
     bwd_tf = f_bwd / (bwd_avg * 1e-3) / 1e12 if not args.fwd_only else None

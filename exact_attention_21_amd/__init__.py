@@ -6,8 +6,8 @@ the C ABI declared in include/fa.h, and every step of the computation runs in
 the library's kernels.  There is no fallback: if libfa.so is missing or the
 device is not gfx950 the calls raise.
 
-Names mirror the C ABI: fa_fwd, fa_bwd (and its three stages fa_bwd_preprocess,
-fa_bwd_dkdv, fa_bwd_dq), fa_fwd_padded, fa_bwd_padded, fa_fwd_dropout,
+Names mirror the C ABI: fa_fwd, fa_bwd (and its stages fa_bwd_preprocess,
+fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dq_preprocess), fa_fwd_padded, fa_bwd_padded, fa_fwd_dropout,
 fa_bwd_dropout, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size,
 fa_bwd_workspace_size, fa_fwd_plan, fa_bwd_plan, fa_status_str.
 fwd(), bwd(), fwd_padded(), bwd_padded(), fwd_dropout(), bwd_dropout() and
@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_dkdv.restype = I
         L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp, Z, vp]
         L.fa_bwd_dq.restype = I
+        L.fa_bwd_dq_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp, Z, vp]
+        L.fa_bwd_dq_preprocess.restype = I
         L.fa_fwd_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, I, vp]
         L.fa_fwd_padded.restype = I
         L.fa_bwd_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, I,
@@ -219,6 +221,22 @@ def fa_bwd_dq(q, k, v, dout, dq, scale: float, causal: bool, workspace, stream=N
                          _stream(stream))
     if rc:
         raise FaError("fa_bwd_dq", rc)
+
+
+def fa_bwd_dq_preprocess(q, k, v, o, dout, lse, dq, scale: float, causal: bool, workspace,
+                         stream=None) -> None:
+    """fa_bwd_dq that also writes the row statistics fa_bwd_dkdv reads (no preprocessed workspace needed)."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)):
+        _check_qkv_like(name, t, q)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    rc = lib().fa_bwd_dq_preprocess(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                    B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
+                                    *_ws(workspace, q), _stream(stream))
+    if rc:
+        raise FaError("fa_bwd_dq_preprocess", rc)
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None):

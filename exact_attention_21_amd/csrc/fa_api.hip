@@ -373,26 +373,55 @@ int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, v
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, void *dq, int B,
-              int H, int N, int d, float scale, int causal, int dtype, void *workspace,
-              size_t workspace_bytes, void *stream) {
-  if (!q || !k || !v || !dout || !dq || !workspace) return FA_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// dQ pass of the staged backward; with o and lse it also computes the row
+// statistics (the preprocessing step) instead of reading them
+int dq_stage(const void *q, const void *k, const void *v, const void *o, const void *dout,
+             const float *lse, void *dq, int B, int H, int N, int d, float scale, int causal,
+             int dtype, void *workspace, size_t workspace_bytes, void *stream) {
   fa::BwdParams p;
   fa_plan_t plan;
   int rc = bwd_setup(B, H, N, N, nullptr, nullptr, d, scale, causal, dtype, workspace,
                      workspace_bytes, &p, &plan);
   if (rc) return rc;
-  if (!all_aligned({q, k, v, dout, dq})) return FA_ERR_ALIGN;
+  const int pre = o != nullptr;
+  if (!all_aligned({q, k, v, dout, dq}) || (pre && !all_aligned({o, lse}))) return FA_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
   p.q = q;
   p.k = k;
   p.v = v;
+  p.o = o;
   p.dout = dout;
+  p.lse = lse;
   p.dq = dq;
-  const hipError_t e = fa::launch_bwd_dq(p, dtype, d, causal, p.n_qtiles * B * H,
+  const hipError_t e = fa::launch_bwd_dq(p, dtype, d, causal, pre, p.n_qtiles * B * H,
                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, void *dq, int B,
+              int H, int N, int d, float scale, int causal, int dtype, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !dout || !dq || !workspace) return FA_ERR_NULL;
+  return dq_stage(q, k, v, nullptr, dout, nullptr, dq, B, H, N, d, scale, causal, dtype, workspace,
+                  workspace_bytes, stream);
+}
+
+int fa_bwd_dq_preprocess(const void *q, const void *k, const void *v, const void *o,
+                         const void *dout, const float *lse, void *dq, int B, int H, int N, int d,
+                         float scale, int causal, int dtype, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !workspace) return FA_ERR_NULL;
+  return dq_stage(q, k, v, o, dout, lse, dq, B, H, N, d, scale, causal, dtype, workspace,
+                  workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -423,9 +452,9 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const v
   p.dk = dk;
   p.dv = dv;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = fa::launch_bwd_pre(p, dtype, d, (long)B * H * Nq, st);
+  // the dQ pass computes the row statistics the dK/dV pass then reads
+  hipError_t e = fa::launch_bwd_dq(p, dtype, d, causal, 1, p.n_qtiles * B * H, st);
   if (e == hipSuccess) e = fa::launch_bwd_dkdv(p, dtype, d, causal, p.n_ktiles * B * H, st);
-  if (e == hipSuccess) e = fa::launch_bwd_dq(p, dtype, d, causal, p.n_qtiles * B * H, st);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -11,7 +11,9 @@
 //   bwd_pre_kernel   -D = -rowsum(dO * O) and LSE * log2(e), fp32 [B][H][Nq]
 //   bwd_dq_kernel    one workgroup per 128 query rows, K/V tiles streamed through
 //                    LDS (the forward's structure): S^T = K Q^T, dP^T = V dO^T,
-//                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T
+//                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T; its PRE variant
+//                    computes -D and LSE * log2(e) itself and stores them, so
+//                    the full backward is two launches: dQ (PRE), then dK/dV
 //   bwd_dkdv_kernel  one workgroup per 128 keys, Q/dO tiles streamed through LDS:
 //                    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS
 // P and dS are recomputed in both passes (two extra tile products compared with
@@ -64,45 +66,54 @@ static_assert(swz_period16<64>() && swz_period16<128>(), "swizzles must repeat e
 #define BWD_DKDV_OCC(D, DROP) ((D) == 64 && !(DROP) ? BWD_DKDV_WAVES_D64 : BWD_DKDV_WAVES_PER_SIMD)
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O) and LSE * log2(e).  16 threads per row.
+// D = rowsum(dO * O) and LSE * log2(e).  One thread per 8 elements of a row.
+// The dQ pass can compute the same statistics itself (PRE): both sides form
+// 8-element partial sums with chunk_dot and add them in one fixed tree, so the
+// two give bitwise-identical D.
 // ---------------------------------------------------------------------------
+namespace {
+// sum of the 8 products of two 16-byte chunks, in a fixed fma order
+template <class T>
+__device__ __forceinline__ float chunk_dot(const u32x4 &a, const u32x4 &b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc = __builtin_fmaf(T::lo(a[j]), T::lo(b[j]), acc);
+    acc = __builtin_fmaf(T::hi(a[j]), T::hi(b[j]), acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float lse_log2(float l) {  // -inf: the row sees no key; +inf makes its P = 0
+  return l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
+}
+}  // namespace
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict__ o,
                                                       const uint16_t *__restrict__ dout,
                                                       const float *__restrict__ lse,
                                                       float *__restrict__ dws,
                                                       float *__restrict__ lse2, long rows) {
-  constexpr int TPR = 16;       // threads per row
-  constexpr int EPT = D / TPR;  // elements per thread (8 or 4)
+  constexpr int TPR = D / 8;  // threads per row: chunk `sub` holds elements 8 sub .. 8 sub + 7
   const long row = (long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int sub = threadIdx.x % TPR;
   float acc = 0.f;
-  if (row < rows) {
-    const uint16_t *op = o + row * D + sub * EPT;
-    const uint16_t *dp = dout + row * D + sub * EPT;
-    if constexpr (EPT == 8) {
-      const u32x4 a = gload16(op), b = gload16(dp);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc += T::lo(a[j]) * T::lo(b[j]) + T::hi(a[j]) * T::hi(b[j]);
-    } else {
-      const u32x2 a = *reinterpret_cast<const u32x2 *>(op), b = *reinterpret_cast<const u32x2 *>(dp);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc += T::lo(a[j]) * T::lo(b[j]) + T::hi(a[j]) * T::hi(b[j]);
-    }
-  }
+  if (row < rows) acc = chunk_dot<T>(gload16(o + row * D + sub * 8), gload16(dout + row * D + sub * 8));
+  // pairwise tree: chunks 8 apart (d = 128), 4, 2, then 1
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
   if (row < rows && sub == 0) {
     dws[row] = -acc;  // -D: the passes start their dP accumulation from it
-    const float l = lse[row];  // -inf: the row sees no key; +inf makes its P = 0
-    lse2[row] = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
+    lse2[row] = lse_log2(lse[row]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // dQ: query-major pass
 // ---------------------------------------------------------------------------
-template <class T, int D, bool CAUSAL, bool DROP>
+// PRE: the pass also computes D and LSE * log2(e) of its rows from O, dO and
+// LSE and stores them for the dK/dV pass (no separate preprocessing kernel)
+template <class T, int D, bool CAUSAL, bool DROP, bool PRE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BWD_DQ_OCC(D, DROP), BWD_DQ_OCC(D, DROP))))
 void bwd_dq_kernel(BwdParams p) {
   constexpr int BN = 32;                // keys per step
@@ -170,15 +181,14 @@ void bwd_dq_kernel(BwdParams p) {
   const float sl2 = p.scale_log2;
 
   // per-lane row statistics; padding rows get lse2 = +inf so that P = 0
-  const float lse2 = qrow < Lq ? p.lse2[(size_t)bh * Nq + qrow] : __builtin_inff();
-  const float ndsum = qrow < Lq ? p.dws[(size_t)bh * Nq + qrow] : 0.f;  // -D
-  // dP^T accumulates from -D (16 loop-invariant registers), so the MFMAs give
-  // dP^T - D; with dropout dP is scaled first, and at d = 64 the registers are
-  // not there (occupancy 4): both start from 0 and subtract
-  constexpr bool DP_FROM_D = !DROP && D == 128;
-  f32x16 dp_init;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) dp_init[r] = DP_FROM_D ? ndsum : 0.f;
+  const size_t srow = (size_t)bh * Nq + qrow;
+  float lse2 = __builtin_inff(), ndsum = 0.f;  // ndsum = -D
+  if constexpr (!PRE) {
+    if (qrow < Lq) {
+      lse2 = p.lse2[srow];
+      ndsum = p.dws[srow];
+    }
+  }
 
   // Q and dO fragments: B operands of S^T = K Q^T and dP^T = V dO^T
   u32x4 qf[ND16], dof[ND16];
@@ -188,6 +198,40 @@ void bwd_dq_kernel(BwdParams p) {
     qf[db] = bload16(rq, off);
     dof[db] = bload16(rdo, off);
   }
+
+  if constexpr (PRE) {
+    // this lane holds chunks 2 db + hi of its row's dO; the partial sums are
+    // added in the preprocessing kernel's tree (chunks 8 apart, 4, 2, 1)
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<const uint16_t *>(p.o) + qoff, (uint32_t)Lq * RB);
+    float part[ND16];
+#pragma unroll
+    for (int db = 0; db < ND16; ++db)
+      part[db] = chunk_dot<T>(bload16(ro, (uint32_t)(qrow * D + db * 16 + hi * 8) * 2), dof[db]);
+    if constexpr (ND16 == 8) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) part[db] += part[db + 4];
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) part[db] += part[db + 2];
+    float dsum = part[0] + part[1];
+    dsum += __shfl_xor(dsum, 32);
+    if (qrow < Lq) {
+      lse2 = lse_log2(p.lse[srow]);
+      ndsum = -dsum;
+      if (hi == 0) {
+        p.dws[srow] = ndsum;
+        p.lse2[srow] = lse2;
+      }
+    }
+  }
+
+  // dP^T accumulates from -D (16 loop-invariant registers), so the MFMAs give
+  // dP^T - D; with dropout dP is scaled first, and at d = 64 the registers are
+  // not there (occupancy 4): both start from 0 and subtract
+  constexpr bool DP_FROM_D = !DROP && D == 128;
+  f32x16 dp_init;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dp_init[r] = DP_FROM_D ? ndsum : 0.f;
 
   // K/V DMA into swizzled slots (K is read both ways, V only as fragments)
   uint32_t dk_off[BPW], dv_off[BPW];
@@ -615,24 +659,27 @@ void bwd_dkdv_kernel(BwdParams p) {
 
 template <class T, int D>
 static hipError_t launch_pre_t(const BwdParams &p, long rows, hipStream_t st) {
-  const int grid = (int)((rows + 15) / 16);
+  constexpr int RPB = 256 / (D / 8);  // rows per workgroup
+  const int grid = (int)((rows + RPB - 1) / RPB);
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(grid), dim3(256), 0, st,
                      reinterpret_cast<const uint16_t *>(p.o),
                      reinterpret_cast<const uint16_t *>(p.dout), p.lse, p.dws, p.lse2, rows);
   return hipGetLastError();
 }
 
-template <class T, int D, bool C>
+template <class T, int D, bool C, bool PRE>
 static hipError_t launch_dq_c(const BwdParams &p, int grid, hipStream_t st) {
   if (p.drop.p8 != 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, C, true>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, C, true, PRE>), dim3(grid), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, C, false>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, C, false, PRE>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 template <class T, int D>
-static hipError_t launch_dq_t(const BwdParams &p, int causal, int grid, hipStream_t st) {
-  return causal ? launch_dq_c<T, D, true>(p, grid, st) : launch_dq_c<T, D, false>(p, grid, st);
+static hipError_t launch_dq_t(const BwdParams &p, int causal, int pre, int grid, hipStream_t st) {
+  if (pre)
+    return causal ? launch_dq_c<T, D, true, true>(p, grid, st) : launch_dq_c<T, D, false, true>(p, grid, st);
+  return causal ? launch_dq_c<T, D, true, false>(p, grid, st) : launch_dq_c<T, D, false, false>(p, grid, st);
 }
 
 template <class T, int D, bool C>
@@ -653,11 +700,12 @@ hipError_t launch_bwd_pre(const BwdParams &p, int dtype, int d, long rows, hipSt
   return d == 128 ? launch_pre_t<F16, 128>(p, rows, st) : launch_pre_t<F16, 64>(p, rows, st);
 }
 
-hipError_t launch_bwd_dq(const BwdParams &p, int dtype, int d, int causal, int grid,
+hipError_t launch_bwd_dq(const BwdParams &p, int dtype, int d, int causal, int pre, int grid,
                          hipStream_t st) {
   if (dtype == 1)
-    return d == 128 ? launch_dq_t<BF16, 128>(p, causal, grid, st) : launch_dq_t<BF16, 64>(p, causal, grid, st);
-  return d == 128 ? launch_dq_t<F16, 128>(p, causal, grid, st) : launch_dq_t<F16, 64>(p, causal, grid, st);
+    return d == 128 ? launch_dq_t<BF16, 128>(p, causal, pre, grid, st)
+                    : launch_dq_t<BF16, 64>(p, causal, pre, grid, st);
+  return d == 128 ? launch_dq_t<F16, 128>(p, causal, pre, grid, st) : launch_dq_t<F16, 64>(p, causal, pre, grid, st);
 }
 
 hipError_t launch_bwd_dkdv(const BwdParams &p, int dtype, int d, int causal, int grid,

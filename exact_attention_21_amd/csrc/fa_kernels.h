@@ -122,8 +122,9 @@ struct BwdParams {
 
 // D = rowsum(dO * O) and LSE * log2(e) (reads p.o, p.dout, p.lse; writes p.dws, p.lse2)
 hipError_t launch_bwd_pre(const BwdParams &p, int dtype, int d, long rows, hipStream_t st);
-// dQ pass (reads q, k, v, dout, dws, lse2; writes dq); grid = n_qtiles * B * H
-hipError_t launch_bwd_dq(const BwdParams &p, int dtype, int d, int causal, int grid,
+// dQ pass (reads q, k, v, dout, dws, lse2; writes dq); grid = n_qtiles * B * H.
+// pre != 0: it computes dws and lse2 itself (reads o and lse, writes dws, lse2)
+hipError_t launch_bwd_dq(const BwdParams &p, int dtype, int d, int causal, int pre, int grid,
                          hipStream_t st);
 // dK/dV pass (reads q, k, v, dout, dws, lse2; writes dk, dv); grid = n_ktiles * B * H
 hipError_t launch_bwd_dkdv(const BwdParams &p, int dtype, int d, int causal, int grid,

@@ -97,16 +97,21 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * The three stages fa_bwd runs on one stream, exposed so that a caller can
- * schedule or time them separately.  They share fa_bwd's argument rules and
- * workspace layout; fa_bwd(...) is exactly
- *   fa_bwd_preprocess -> fa_bwd_dkdv -> fa_bwd_dq
- * (the last two only read the workspace and may run in either order).
+ * The stages of the backward, exposed so that a caller can schedule or time
+ * them separately.  They share fa_bwd's argument rules and workspace layout.
+ * Two orders give results bitwise equal to fa_bwd's (which runs the second):
+ *   fa_bwd_preprocess -> fa_bwd_dkdv and fa_bwd_dq (these two in either order)
+ *   fa_bwd_dq_preprocess -> fa_bwd_dkdv
  *
  * fa_bwd_preprocess: reads o, dout and lse; writes -D_i = -sum_c dO_ic O_ic and
  *   lse * log2(e) (fp32) into the workspace.
  * fa_bwd_dkdv: recomputes P and dS key-block by key-block; writes dk and dv.
- * fa_bwd_dq: recomputes P and dS query-block by query-block; writes dq.
+ *   Reads the workspace written by either preprocessing stage.
+ * fa_bwd_dq: recomputes P and dS query-block by query-block; writes dq.  Reads
+ *   the workspace written by fa_bwd_preprocess.
+ * fa_bwd_dq_preprocess: fa_bwd_dq that computes the row statistics itself from
+ *   o, dout and lse (it needs no preprocessed workspace) and stores them in the
+ *   workspace, as fa_bwd_preprocess does, for fa_bwd_dkdv.
  */
 int fa_bwd_preprocess(const void *o, const void *dout, const float *lse, int B, int H,
                       int N, int d, int dtype, void *workspace, size_t workspace_bytes,
@@ -117,6 +122,10 @@ int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, v
 int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, void *dq,
               int B, int H, int N, int d, float scale, int causal, int dtype,
               void *workspace, size_t workspace_bytes, void *stream);
+int fa_bwd_dq_preprocess(const void *q, const void *k, const void *v, const void *o,
+                         const void *dout, const float *lse, void *dq, int B, int H, int N,
+                         int d, float scale, int causal, int dtype, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /*
  * Padded batches and cross-attention.  "Flash Attention application"

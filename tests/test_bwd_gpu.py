@@ -84,20 +84,42 @@ def test_gradients_bitwise_repeatable(gpu):
         assert torch.equal(a, b)
 
 
-def test_staged_entry_points_match_fa_bwd(gpu):
+@pytest.mark.parametrize("d,dt", [(128, "f16"), (64, "bf16")])
+def test_staged_entry_points_match_fa_bwd(gpu, d, dt):
     import torch
-    qb, kb, vb, dob = fa_inputs.qkv_bits(1, 4, 300, 128, "f16", seed=92, with_dout=True)
-    q, k, v, do = (to_device(x, "f16", gpu) for x in (qb, kb, vb, dob))
+    B, H, N = 1, 4, 300
+    qb, kb, vb, dob = fa_inputs.qkv_bits(B, H, N, d, dt, seed=92, with_dout=True)
+    q, k, v, do = (to_device(x, dt, gpu) for x in (qb, kb, vb, dob))
     o, lse = fa.fwd(q, k, v, causal=True)
     ref = fa.bwd(q, k, v, o, do, lse, causal=True)
-    ws = torch.empty(fa.fa_bwd_workspace_size(1, 4, 300, 128), dtype=torch.uint8, device=gpu)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=gpu)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    scale = 1 / math.sqrt(128)
+    scale = 1 / math.sqrt(d)
     fa.fa_bwd_preprocess(o, do, lse, ws)
     fa.fa_bwd_dq(q, k, v, do, dq, scale, True, ws)
     fa.fa_bwd_dkdv(q, k, v, do, dk, dv, scale, True, ws)
     torch.cuda.synchronize()
     for a, b in zip((dq, dk, dv), ref):
+        assert torch.equal(a, b)
+
+    # the workspace holds -D and LSE*log2(e), fp32 [B][H][N] each, the second
+    # at the first 256-byte boundary after the first
+    rows = B * H * N
+    second = (rows * 4 + 255) // 256 * 256
+
+    def stats(w):
+        return w[: rows * 4].clone(), w[second: second + rows * 4].clone()
+
+    pre = stats(ws)
+    # the dQ pass that computes the statistics itself writes the same values
+    ws.fill_(0xFF)
+    dq2, dk2, dv2 = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    fa.fa_bwd_dq_preprocess(q, k, v, o, do, lse, dq2, scale, True, ws)
+    fa.fa_bwd_dkdv(q, k, v, do, dk2, dv2, scale, True, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(stats(ws), pre):
+        assert torch.equal(a, b)
+    for a, b in zip((dq2, dk2, dv2), ref):
         assert torch.equal(a, b)
 
 
