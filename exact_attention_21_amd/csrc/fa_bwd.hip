@@ -229,6 +229,9 @@ void bwd_dq_kernel(BwdParams p) {
   // dP^T - D; with dropout dP is scaled first, and at d = 64 the registers are
   // not there (occupancy 4): both start from 0 and subtract
   constexpr bool DP_FROM_D = !DROP && D == 128;
+  // K^T column blocks read before the softmax (d = 128 without dropout: the
+  // other variants have no registers to spare)
+  constexpr int KT_EARLY = DROP || D != 128 ? 0 : (BWD_DQ_KT_EARLY < ND32 ? BWD_DQ_KT_EARLY : ND32);
   f32x16 dp_init;
 #pragma unroll
   for (int r = 0; r < 16; ++r) dp_init[r] = DP_FROM_D ? ndsum : 0.f;
@@ -292,6 +295,19 @@ void bwd_dq_kernel(BwdParams p) {
     }
     // P^T = exp2(scale log2e S - LSE log2e), masked; dS^T = P^T (dP^T - D),
     // the difference already formed by the MFMAs
+    // K^T operands of the first KT_EARLY column blocks of dQ^T += K^T dS^T,
+    // read now: they do not depend on the softmax, and reads issued after the
+    // mask branch could not be moved above it
+    u32x4 kt[KT_EARLY > 0 ? KT_EARLY : 1][2];
+#pragma unroll
+    for (int c = 0; c < KT_EARLY; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const char *kk = ks + kb * 16 * RB;
+        const u32x2 a0 = lds_read_tr4(kk + (t_base[0] ^ (uint32_t)(64 * c)));
+        const u32x2 a1 = lds_read_tr4(kk + (t_base[1] ^ (uint32_t)(64 * c)));
+        kt[c][kb] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+      }
     const int j0 = t * BN;
     const bool need_mask = (CAUSAL && j0 + BN - 1 > wr0 + shift) || (j0 + BN > Lk);
     // dropout: dP is masked and scaled (dS = P (Z dP - D), Z = keep * 256 / (256 - p8))
@@ -326,11 +342,15 @@ void bwd_dq_kernel(BwdParams p) {
     for (int c = 0; c < ND32; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const char *kk = ks + kb * 16 * RB;
-        const u32x2 a0 = lds_read_tr4(kk + (t_base[0] ^ (uint32_t)(64 * c)));
-        const u32x2 a1 = lds_read_tr4(kk + (t_base[1] ^ (uint32_t)(64 * c)));
         const u32x4 b = {dsk[4 * kb], dsk[4 * kb + 1], dsk[4 * kb + 2], dsk[4 * kb + 3]};
-        dqacc[c] = T::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, b, dqacc[c]);
+        if (c < KT_EARLY) {
+          dqacc[c] = T::mma(kt[c < KT_EARLY ? c : 0][kb], b, dqacc[c]);
+        } else {
+          const char *kk = ks + kb * 16 * RB;
+          const u32x2 a0 = lds_read_tr4(kk + (t_base[0] ^ (uint32_t)(64 * c)));
+          const u32x2 a1 = lds_read_tr4(kk + (t_base[1] ^ (uint32_t)(64 * c)));
+          dqacc[c] = T::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, b, dqacc[c]);
+        }
       }
     }
     wait_vmcnt<(NS - 2) * DMA_PER_STEP>();  // tiles for step t + 1 have landed

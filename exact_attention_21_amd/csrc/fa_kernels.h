@@ -100,6 +100,9 @@ constexpr int BWD_DKDV_BM = 32;
 #ifndef BWD_DQ_NSLOT_D128
 #define BWD_DQ_NSLOT_D128 3  // dQ pass K/V ring slots at d = 128 (loads run NSLOT - 1 steps ahead)
 #endif
+#ifndef BWD_DQ_KT_EARLY
+#define BWD_DQ_KT_EARLY 4  // dQ pass (d = 128, no dropout): K^T column blocks read before the softmax
+#endif
 #ifndef BWD_DKDV_NSLOT
 #define BWD_DKDV_NSLOT 2
 #endif
