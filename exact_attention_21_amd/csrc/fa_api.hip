@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -108,6 +109,25 @@ SplitPlan split_plan(int B, int H, int Nq, int Nk, int d) {
     }
     if (fill >= 0.95) break;
   }
+  return sp;
+}
+
+// Decode (Nq = 1): partials per head = 4 waves x workgroups per head, sized so
+// that B*H heads give about 4096 waves (one per SIMD slot at occupancy 4), each
+// over at least 256 keys; chunks are whole tiles.
+SplitPlan decode_plan(int B, int H, int Nk, int d) {
+  constexpr long long kWaves = 4096, kMinKeys = 256;
+  const long long heads = (long long)B * H;
+  const long long tk = fa::fwd_decode_tile(d);
+  long long wg = (kWaves + 4 * heads - 1) / (4 * heads);
+  wg = std::min(wg, ((long long)Nk + 4 * kMinKeys - 1) / (4 * kMinKeys));
+  wg = std::max(wg, 1LL);
+  const long long per = ((long long)Nk + 4 * wg - 1) / (4 * wg);
+  SplitPlan sp;
+  sp.bm = 1;
+  sp.n_qtiles = 1;
+  sp.nsplit = (int)(4 * wg);
+  sp.chunk = (int)std::max(tk, (per + tk - 1) / tk * tk);
   return sp;
 }
 
@@ -219,7 +239,7 @@ int fa_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *
 size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d) {
   if (check_common(B, H, Nq, d, 0, FA_BF16) != FA_OK || check_common(B, H, Nk, d, 0, FA_BF16) != FA_OK)
     return 0;
-  return split_workspace_bytes(B, H, Nq, d, split_plan(B, H, Nq, Nk, d));
+  return split_workspace_bytes(B, H, Nq, d, Nq == 1 ? decode_plan(B, H, Nk, d) : split_plan(B, H, Nq, Nk, d));
 }
 
 int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -232,8 +252,9 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
   rc = check_common(B, H, Nk, d, causal, dtype);
   if (rc) return rc;
   if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
-  const SplitPlan sp = split_plan(B, H, Nq, Nk, d);
-  const long long grid = (long long)sp.n_qtiles * sp.nsplit * B * H;
+  const bool decode = Nq == 1;
+  const SplitPlan sp = decode ? decode_plan(B, H, Nk, d) : split_plan(B, H, Nq, Nk, d);
+  const long long grid = decode ? (long long)B * H * (sp.nsplit / 4) : (long long)sp.n_qtiles * sp.nsplit * B * H;
   if (grid > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(workspace))
@@ -260,7 +281,8 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
   p.opart = reinterpret_cast<float *>(ws);
   p.lpart = reinterpret_cast<float *>(ws + align256(prows * d * sizeof(float)));
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = fa::launch_fwd_split(p, dtype, d, causal, (int)grid, st);
+  hipError_t e = decode ? fa::launch_fwd_decode(p, dtype, d, (int)grid, st)
+                        : fa::launch_fwd_split(p, dtype, d, causal, (int)grid, st);
   if (e == hipSuccess) e = fa::launch_fwd_combine(p, dtype, d, (long)B * H * Nq, st);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

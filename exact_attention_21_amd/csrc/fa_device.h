@@ -17,6 +17,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace fa {
@@ -46,6 +47,10 @@ struct BF16 {
   }
   static __device__ __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
   static __device__ __forceinline__ float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+  // c + a.lo * b.lo + a.hi * b.hi (v_dot2_f32_bf16)
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+  }
 };
 
 struct F16 {
@@ -63,6 +68,10 @@ struct F16 {
   }
   static __device__ __forceinline__ float hi(uint32_t u) {
     return (float)__builtin_bit_cast(f16x2, u)[1];
+  }
+  // c + a.lo * b.lo + a.hi * b.hi (v_dot2_f32_f16)
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
   }
 };
 
@@ -84,6 +93,23 @@ __device__ __forceinline__ float sum_xhalf(float x) {
   uint32_t u = __float_as_uint(x);
   auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over each group of N consecutive lanes (N = 8 or 16), left in every lane
+// of the group: DPP swaps with lane ^ 1 and lane ^ 2, then the mirror images
+// within 8 and within 16 lanes.  Both lanes of every exchange add the same two
+// values, so the group's lanes end with bitwise-equal sums.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, true));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (N == 16) x += dpp(x, std::integral_constant<int, 0x140>{});  // row_mirror
+  return x;
 }
 
 __device__ __forceinline__ u32x4 lds_read16(const char *p) {

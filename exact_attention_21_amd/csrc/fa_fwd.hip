@@ -519,6 +519,109 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float *__restric
 }
 
 // ---------------------------------------------------------------------------
+// Decode: one query row per (batch, head) against a long K/V.  Per head this
+// is two matrix-vector products (scores = K q, o = V^T p) that read every K
+// and V byte once and do 2 FLOP per byte: bound by HBM, not by the matrix
+// cores, and an MFMA tile would be 31/32 padding.  So the kernel streams K
+// and V through registers with wave-wide 16-byte loads and works on the
+// vector ALUs: v_dot2 for the scores, FMAs for the output.
+//
+// Lane roles: a row of d 16-bit values is LPK = d/8 lanes of 16 bytes, so one
+// load covers KPL = 64/LPK consecutive key rows; lane = (key slot g, column
+// chunk u).  Each wave takes its own chunk of p.chunk keys with its own online
+// softmax (running max in the log2 domain, rescale of the running sum and
+// output at every tile) and writes one partial: the chunk's normalised output
+// and LSE, merged by fwd_combine_kernel like the split forward's partials.
+// p.nsplit = partials per head = 4 x workgroups per head.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(256) void fwd_decode_kernel(FwdParams p) {
+  constexpr int RB = D * 2;      // bytes per row
+  constexpr int LPK = D / 8;     // lanes per key row
+  constexpr int KPL = 64 / LPK;  // key rows per load
+  constexpr int NI = 8;          // loads per tensor per tile
+  constexpr int TK = NI * KPL;   // keys per tile: 32 (d = 128) or 64 (d = 64)
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane / LPK, u = lane % LPK;
+  const int wg_per_head = p.nsplit / 4;
+  const int bh = blockIdx.x / wg_per_head;
+  const int split = (blockIdx.x % wg_per_head) * 4 + w;
+  int Lq, Lk;
+  seq_lengths(p.seq, bh / p.seq.H, Lq, Lk);
+  // the single query sees keys [0, Lk) (causal changes nothing when Nq = 1);
+  // a padding row (Lq = 0) sees none
+  const int j0 = split * p.chunk;
+  const int j1 = Lq > 0 ? min(j0 + p.chunk, Lk) : 0;
+  const size_t koff = (size_t)bh * (size_t)p.seq.Nk * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + koff, (uint32_t)Lk * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + koff, (uint32_t)Lk * RB);
+  const u32x4 qv = gload16(reinterpret_cast<const uint16_t *>(p.q) + (size_t)bh * D + u * 8);
+  const float sl2 = p.scale_log2;
+
+  float m = -__builtin_inff(), l = 0.f;  // running max (log2 domain) and this key slot's sum
+  float o[8] = {};                       // columns 8u .. 8u + 7, this key slot's keys
+  for (int t0 = j0; t0 < j1; t0 += TK) {
+    u32x4 kv[NI], vv[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t off = (uint32_t)((t0 + i * KPL + g) * RB + u * 16);  // rows past Lk read 0
+      kv[i] = bload16(rk, off);
+      vv[i] = bload16(rv, off);
+    }
+    // scores of the tile's keys (key t0 + i KPL + g), log2 domain, masked past j1
+    float s[NI];
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float dt = T::dot2(kv[i][0], qv[0], 0.f);
+      dt = T::dot2(kv[i][1], qv[1], dt);
+      dt = T::dot2(kv[i][2], qv[2], dt);
+      dt = T::dot2(kv[i][3], qv[3], dt);
+      dt = group_sum<LPK>(dt);
+      s[i] = t0 + i * KPL + g < j1 ? dt * sl2 : -__builtin_inff();
+      mt = fmaxf(mt, s[i]);
+    }
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off, 64));
+    const float mn = fmaxf(m, mt);
+    if (mn == -__builtin_inff()) continue;  // wave-uniform: no visible key yet
+    const float alpha = fast_exp2(m - mn);  // 0 while m = -inf
+    m = mn;
+    float ls = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float pr = fast_exp2(s[i] - mn);  // masked: exp2(-inf) = 0
+      ls += pr;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        o[2 * c] = __builtin_fmaf(pr, T::lo(vv[i][c]), o[2 * c]);
+        o[2 * c + 1] = __builtin_fmaf(pr, T::hi(vv[i][c]), o[2 * c + 1]);
+      }
+    }
+    l = l * alpha + ls;
+  }
+  // totals over the key slots (lanes with the same column chunk)
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    l += __shfl_xor(l, off, 64);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] += __shfl_xor(o[c], off, 64);
+  }
+  const bool live = l > 0.f;
+  const size_t prow = (size_t)bh * p.nsplit + split;  // Nq = 1
+  if (g == 0) {
+    const float inv = live ? 1.f / l : 0.f;
+    float *op = p.opart + prow * D + u * 8;
+    *reinterpret_cast<f32x4 *>(op) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    *reinterpret_cast<f32x4 *>(op + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+  }
+  if (lane == 0) p.lpart[prow] = live ? (m + fast_log2(l)) * 0.6931471805599453f : -__builtin_inff();
+}
+
+// ---------------------------------------------------------------------------
 // instantiation table
 // ---------------------------------------------------------------------------
 
@@ -545,6 +648,17 @@ hipError_t launch_fwd_split(const FwdParams &p, int dtype, int d, int causal, in
                     : (causal ? launch_split_t<BF16, 64, true>(p, grid, st) : launch_split_t<BF16, 64, false>(p, grid, st));
   return d == 128 ? (causal ? launch_split_t<F16, 128, true>(p, grid, st) : launch_split_t<F16, 128, false>(p, grid, st))
                   : (causal ? launch_split_t<F16, 64, true>(p, grid, st) : launch_split_t<F16, 64, false>(p, grid, st));
+}
+
+template <class T, int D>
+static hipError_t launch_decode_t(const FwdParams &p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((fwd_decode_kernel<T, D>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_decode(const FwdParams &p, int dtype, int d, int grid, hipStream_t st) {
+  if (dtype == 1) return d == 128 ? launch_decode_t<BF16, 128>(p, grid, st) : launch_decode_t<BF16, 64>(p, grid, st);
+  return d == 128 ? launch_decode_t<F16, 128>(p, grid, st) : launch_decode_t<F16, 64>(p, grid, st);
 }
 
 template <class T, int D>

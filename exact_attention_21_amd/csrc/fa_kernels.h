@@ -140,5 +140,10 @@ hipError_t launch_fwd(const FwdParams &p, int dtype, int d, int causal, int qb, 
 hipError_t launch_fwd_split(const FwdParams &p, int dtype, int d, int causal, int grid,
                             hipStream_t st);
 hipError_t launch_fwd_combine(const FwdParams &p, int dtype, int d, long rows, hipStream_t st);
+// decode forward (Nq = 1): one partial per wave, p.nsplit partials per head
+// (a multiple of 4), p.chunk keys each (a multiple of fwd_decode_tile(d));
+// grid = B * H * nsplit / 4; the partials are merged by launch_fwd_combine
+constexpr int fwd_decode_tile(int d) { return d == 128 ? 32 : 64; }
+hipError_t launch_fwd_decode(const FwdParams &p, int dtype, int d, int grid, hipStream_t st);
 
 }  // namespace fa

@@ -198,7 +198,8 @@ int fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o,
  * against a key/value cache; the xformers page's decoding benchmark and the
  * first-token latency scenario of "Flash Attention application").  The keys
  * of each (batch, head, query tile) are cut into chunks that run as separate
- * workgroups, so that B*H*ceil(Nq/128) small does not leave the GPU idle; each
+ * workgroups (with Nq = 1: separate waves of a streaming kernel on the vector
+ * ALUs), so that B*H*ceil(Nq/128) small does not leave the GPU idle; each
  * chunk writes its normalised partial output and log-sum-exp, and a second
  * kernel merges the chunks with the LSE merge rule of the handbook's
  * engineering-implementation pseudocode:
