@@ -149,16 +149,8 @@ void bwd_dq_kernel(BwdParams p) {
   int bh, qt;
   {
     const int nq = p.n_qtiles;
-    const int bid = blockIdx.x;
     int r;
-    if (p.xcd_grouped) {
-      const int x = bid & 7, kk = bid >> 3;
-      bh = x + 8 * (kk / nq);
-      r = kk % nq;
-    } else {
-      bh = bid / nq;
-      r = bid % nq;
-    }
+    grid_tile((int)blockIdx.x, (int)gridDim.x / nq, nq, p.xcd_grouped, CAUSAL ? FA_CAUSAL_GROUP : 1, bh, r);
     qt = CAUSAL ? nq - 1 - r : r;  // causal: longest rows first
   }
   const int i0 = qt * BM;
@@ -438,16 +430,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   int bh, kt;
   {
     const int nk = p.n_ktiles;
-    const int bid = blockIdx.x;
-    if (p.xcd_grouped) {
-      const int x = bid & 7, kk = bid >> 3;
-      bh = x + 8 * (kk / nk);
-      kt = kk % nk;
-    } else {
-      bh = bid / nk;
-      kt = bid % nk;
-    }
     // causal: key tile 0 sees every query tile, so ascending order is heavy-first
+    grid_tile((int)blockIdx.x, (int)gridDim.x / nk, nk, p.xcd_grouped, CAUSAL ? FA_CAUSAL_GROUP : 1, bh, kt);
   }
   const int j0 = kt * BN;
   const int kw0 = j0 + 32 * w;

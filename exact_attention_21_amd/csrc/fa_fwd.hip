@@ -151,15 +151,9 @@ void fwd_kernel(FwdParams p) {
   {
     const int nq = p.n_qtiles;
     const int bid = SPLIT ? (int)(blockIdx.x / (unsigned)p.nsplit) : (int)blockIdx.x;
+    const int heads = (int)(gridDim.x / (SPLIT ? (unsigned)p.nsplit : 1u)) / nq;
     int r;
-    if (p.xcd_grouped) {  // heads of one XCD (bid % 8) run together: K/V stay in its L2
-      const int x = bid & 7, kk = bid >> 3;
-      bh = x + 8 * (kk / nq);
-      r = kk % nq;
-    } else {
-      bh = bid / nq;
-      r = bid % nq;
-    }
+    grid_tile(bid, heads, nq, p.xcd_grouped, CAUSAL ? FA_CAUSAL_GROUP : 1, bh, r);
     qt = CAUSAL ? nq - 1 - r : r;  // causal: longest rows first
   }
   const int i0 = qt * BM;

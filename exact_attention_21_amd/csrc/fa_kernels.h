@@ -62,6 +62,13 @@ struct DropoutSpec {
   float scale;
 };
 
+// Causal grids: heads per dispatch group (see grid_tile).  Pairs: the grid
+// ends on shorter tiles than with one head at a time, while only two heads'
+// K/V per XCD are in use at once.
+#ifndef FA_CAUSAL_GROUP
+#define FA_CAUSAL_GROUP 2
+#endif
+
 struct FwdParams {
   const void *q, *k, *v;
   void *o;

@@ -22,6 +22,8 @@ CASES = {
     "spec_q7_k2048": (2, 4, 7, 2048, None, [2048, 900]),
     "prefill_q300_k9000": (1, 2, 300, 9000, [300], [9000]),
     "decode_q1_k40000": (1, 4, 1, 40000, None, None),
+    "decode_q1_padding_row": (2, 4, 1, 3000, [1, 0], [3000, 2999]),
+    "decode_q1_k5": (1, 2, 1, 5, None, None),
 }
 
 
