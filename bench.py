@@ -46,9 +46,9 @@ WORKLOAD = dict(name="c3_fwd_bwd_causal_n8192_d128_bf16", B=4, H=32, N=8192, d=1
 # profiles/fwd_bwd_causal_n8192_d128_bf16_hbm_traffic.md).  Valid only for the
 # kernel sources they were taken on: the hash of those sources must match.
 MEASURED_TRAFFIC = {
-    "source_sha256_16": "88865b354d6cab9a",
-    "bytes": {"fwd_kernel": 2.1855e9, "bwd_dq_kernel": 2.4053e9,
-              "bwd_dkdv_kernel": 1.9198e9},
+    "source_sha256_16": "821dccf51117dbbd",
+    "bytes": {"fwd_kernel": 3.7179e9, "bwd_dq_kernel": 2.3937e9,
+              "bwd_dkdv_kernel": 1.9104e9},
 }
 KERNEL_SOURCES = ["exact_attention_21_amd/csrc/fa_bwd.hip", "exact_attention_21_amd/csrc/fa_fwd.hip",
                   "exact_attention_21_amd/csrc/fa_device.h", "exact_attention_21_amd/csrc/fa_kernels.h",

@@ -115,20 +115,30 @@ __device__ __forceinline__ float group_sum(float x) {
 // Workgroup -> (head, tile rank) for a 1-D grid of heads x ntiles workgroups.
 // With xcd_grouped (heads a multiple of 8) workgroup bid runs on XCD bid % 8
 // and only heads bh with bh % 8 == bid % 8 go there.  The heads of an XCD are
-// taken in groups of `group`; within a group every head's rank-0 tile comes
-// first, then every rank-1 tile, and so on.  group = 1: a head's tiles are
-// consecutive, so they run together and share its K/V in L2; larger groups
-// interleave more heads (more L2 traffic) but, with rank 0 the longest tile
-// of a causal mask, end the grid on shorter tiles.
+// taken in groups of `group`, and its last `tail` heads form one group of
+// their own; within a group every head's rank-0 tile comes first, then every
+// rank-1 tile, and so on.  group = 1: a head's tiles are consecutive, so they
+// run together and share its K/V in L2; larger groups interleave more heads
+// (more L2 traffic) but, with rank 0 the longest tile of a causal mask, end
+// the grid on shorter tiles; the tail group evens out the end of the grid.
 __device__ __forceinline__ void grid_tile(int bid, int heads, int ntiles, bool xcd_grouped, int group,
-                                          int &bh, int &rank) {
+                                          int tail, int &bh, int &rank) {
   const int lanes = xcd_grouped ? 8 : 1;                 // heads interleaved across XCDs
   const int x = xcd_grouped ? (bid & 7) : 0, kk = xcd_grouped ? (bid >> 3) : bid;
   const int hpx = heads / lanes;                         // heads of this XCD (or of the grid)
-  const int gi = kk / (group * ntiles), idx = kk % (group * ntiles);
-  const int gsz = min(group, hpx - gi * group);          // the last group may be smaller
-  rank = idx / gsz;
-  bh = x + lanes * (gi * group + idx % gsz);
+  const int nt = min(max(tail, 0), hpx), nrest = hpx - nt;
+  int h;
+  if (kk < nrest * ntiles) {
+    const int gi = kk / (group * ntiles), idx = kk % (group * ntiles);
+    const int gsz = min(group, nrest - gi * group);      // the last group may be smaller
+    rank = idx / gsz;
+    h = gi * group + idx % gsz;
+  } else {
+    const int idx = kk - nrest * ntiles;
+    rank = idx / nt;
+    h = nrest + idx % nt;
+  }
+  bh = x + lanes * h;
 }
 
 __device__ __forceinline__ u32x4 lds_read16(const char *p) {

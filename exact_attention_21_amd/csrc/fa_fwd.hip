@@ -153,7 +153,11 @@ void fwd_kernel(FwdParams p) {
     const int bid = SPLIT ? (int)(blockIdx.x / (unsigned)p.nsplit) : (int)blockIdx.x;
     const int heads = (int)(gridDim.x / (SPLIT ? (unsigned)p.nsplit : 1u)) / nq;
     int r;
-    grid_tile(bid, heads, nq, p.xcd_grouped, CAUSAL ? FA_CAUSAL_GROUP : 1, bh, r);
+    // causal: heads in pairs, and the last heads (two rounds of the FWD_OCC
+    // workgroups per CU of an XCD's 32 CUs, or of all 256 when the heads are
+    // not grouped per XCD) in one group, so that the grid ends on short tiles
+    grid_tile(bid, heads, nq, p.xcd_grouped, CAUSAL ? FA_CAUSAL_GROUP : 1,
+              CAUSAL ? causal_tail_heads(nq, (p.xcd_grouped ? 32 : 256) * FWD_OCC(D, QB, DROP)) : 0, bh, r);
     qt = CAUSAL ? nq - 1 - r : r;  // causal: longest rows first
   }
   const int i0 = qt * BM;

@@ -68,6 +68,11 @@ struct DropoutSpec {
 #ifndef FA_CAUSAL_GROUP
 #define FA_CAUSAL_GROUP 2
 #endif
+// Heads of the final dispatch group of an XCD that holds `slots` workgroups
+// at once: enough tiles for two rounds of its slots.
+__host__ __device__ constexpr int causal_tail_heads(int ntiles, int slots) {
+  return (2 * slots + ntiles - 1) / ntiles;
+}
 
 struct FwdParams {
   const void *q, *k, *v;
