@@ -2,9 +2,10 @@
 """Attention throughput on one MI355X: fused forward + recompute backward.
 
 One step = one pass of the whole hot path over one batch: fa_fwd (O, LSE) then
-the backward's three stages (D = rowsum(dO*O), the dK/dV pass, the dQ pass) on the
-causal workload B=4, H=32, N=8192, d=128, bf16, with Q, K, V, dO i.i.d. N(0,1)
-from a fixed seed, all resident in HBM before timing starts.
+the backward's two passes as fa_bwd runs them (the dQ pass, which also forms
+D = rowsum(dO*O), then the dK/dV pass) on the causal workload B=4, H=32, N=8192,
+d=128, bf16, with Q, K, V, dO i.i.d. N(0,1) from a fixed seed, all resident in
+HBM before timing starts.
 
 FLOP convention: 4*B*H*N^2*d for the forward, halved when causal; the backward
 counts 2.5x the forward.  `value` is (forward + backward FLOP) / step time.
