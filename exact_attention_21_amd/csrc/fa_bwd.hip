@@ -126,10 +126,10 @@ void bwd_dq_kernel(BwdParams p) {
   constexpr int ND16 = D / 16, ND32 = D / 32;
   static_assert(BPW >= 1 && BM == 128, "tile shape");
 
-  // two-slot K and V rings, one LDS object per slot (the compiler can then tell
-  // the slot being loaded from the slot being read)
-  // ring slots (loads run NS - 1 steps ahead): three at d = 128 (cross-
-  // attention's backward 1.3 % faster, square shapes unchanged), two at d = 64
+  // K and V rings of NS slots, one LDS object per slot (the compiler can then
+  // tell the slot being loaded from the slot being read); loads run NS - 1
+  // steps ahead: three slots at d = 128 (cross-attention's backward 1.3 %
+  // faster, square shapes unchanged), two at d = 64
   constexpr int NS = D == 128 ? BWD_DQ_NSLOT_D128 : 2;
   static_assert(NS == 2 || NS == 3, "two- or three-slot rings");
   __shared__ __attribute__((aligned(1024))) char k_slot0[TB];
