@@ -105,3 +105,26 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
                 assert "liboracle" not in text and "oracle.c" not in text, f
+
+
+def _align256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,H,Nk,d,partials", [
+    (32, 32, 16384, 128, 4),   # 1024 heads: one workgroup (4 waves, 4 partials) per head
+    (1, 4, 40000, 128, 160),   # 4 heads: 40 workgroups per head, chunks of >= 256 keys
+    (1, 2, 5, 64, 4),          # fewer keys than one tile: a single workgroup per head
+])
+def test_decode_split_workspace(B, H, Nk, d, partials):
+    # one query row: fp32 partial output rows and LSEs, one per wave of the decode kernel
+    rows = B * H * partials
+    assert fa.fa_fwd_splitkv_workspace_size(B, H, 1, Nk, d) == _align256(rows * d * 4) + _align256(rows * 4)
+
+
+def test_split_workspace_covers_every_chunk():
+    for B, H, Nq, Nk, d in [(2, 4, 7, 2048, 128), (1, 2, 300, 9000, 64), (8, 16, 128, 65536, 128)]:
+        ws = fa.fa_fwd_splitkv_workspace_size(B, H, Nq, Nk, d)
+        assert ws >= B * H * Nq * d * 4 + B * H * Nq * 4  # at least one chunk
+        assert ws % 256 == 0
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1, 16, 96) == 0  # unsupported head size
