@@ -81,3 +81,26 @@ def test_splitkv_workspace_checked(gpu):
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd_splitkv(q, k, k, o, lse, None, None, 0.125, False, ws)
     assert e.value.status == 6  # FA_ERR_WORKSPACE
+
+
+def test_decode_full_size_sampled_heads(gpu):
+    # the benchmark's decode call: B=32 H=32, one query per (batch, head) over
+    # 16384 keys, bf16, causal (one workgroup of four partials per head); inputs
+    # N(0,1) drawn on the device from a fixed seed, sampled heads checked
+    import torch
+    B, H, Nk, d = 32, 32, 16384, 128
+    say(f"[splitkv full] decode B={B} H={H} Nk={Nk}")
+    gen = torch.Generator(device=gpu).manual_seed(4950)
+    draw = lambda n: torch.randn((B, H, n, d), generator=gen, device=gpu, dtype=torch.float32).to(torch.bfloat16)
+    q, k, v = draw(1), draw(Nk), draw(Nk)
+    o, lse = fa.fwd_splitkv(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    scale = float(np.float32(1 / math.sqrt(d)))
+    worst_o = worst_l = 0.0
+    for b, h in [(0, 0), (0, 31), (13, 7), (31, 0), (31, 31)]:
+        sub = [to_host_f64(x[b:b + 1, h:h + 1]) for x in (q, k, v)]
+        ro, rl = oracle.fwd_padded(*sub, scale, True, None, None)
+        worst_o = max(worst_o, max_abs(to_host_f64(o[b:b + 1, h:h + 1]), ro))
+        worst_l = max(worst_l, max_abs(to_host_f64(lse[b:b + 1, h:h + 1]), rl))
+    say(f"    5 heads: O max-abs {worst_o:.3e}  LSE max-abs {worst_l:.3e}")
+    assert worst_o <= TOL_O["bf16"] and worst_l <= TOL_LSE
