@@ -461,6 +461,15 @@ void bwd_dkdv_kernel(BwdParams p) {
     kf[db] = bload16(rk, off);
     vf[db] = bload16(rv, off);
   }
+  // With dropout at d = 128 the last NVL V fragments live in LDS (one 16-byte
+  // slot per thread, read back each step): the registers they free keep the
+  // compiler from spilling, whose scratch reloads would wait on the tile DMA
+  // in flight (both count in vmcnt) and so undo the prefetch.
+  constexpr int NVL = DROP && D == 128 ? BWD_DKDV_DROP_VF_LDS : 0;
+  __shared__ __attribute__((aligned(16))) u32x4 vf_lds[NVL > 0 ? NVL : 1][256];
+#pragma unroll
+  for (int j = 0; j < NVL; ++j) vf_lds[j][tid] = vf[ND16 - NVL + j];
+  auto vfrag = [&](int db) -> u32x4 { return db >= ND16 - NVL ? vf_lds[db - (ND16 - NVL)][tid] : vf[db]; };
 
   // query tiles with valid rows that see a key of this block (none if all its keys are padding)
   const int nqt = j0 >= Lk ? 0 : (Lq + BM - 1) / BM;
@@ -549,7 +558,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int db = 0; db < ND16; ++db) {
       const uint32_t fa = f_base ^ (uint32_t)(32 * db);
       s = T::mma(lds_read16(qs + fa), kf[db], s);
-      dp = T::mma(lds_read16(ds + fa), vf[db], dp);
+      dp = T::mma(lds_read16(ds + fa), vfrag(db), dp);
     }
     const bool need_mask = CAUSAL && q0 + shift < kw0 + 31;
     // dropout: dV takes P * keep (scaled in the epilogue), dS = P (Z dP - D)

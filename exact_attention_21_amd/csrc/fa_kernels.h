@@ -117,6 +117,9 @@ constexpr int BWD_DKDV_BM = 32;
 #ifndef BWD_DQ_KT_EARLY
 #define BWD_DQ_KT_EARLY 4  // dQ pass (d = 128, no dropout): K^T column blocks read before the softmax
 #endif
+#ifndef BWD_DKDV_DROP_VF_LDS
+#define BWD_DKDV_DROP_VF_LDS 3  // dK/dV pass with dropout, d = 128: V fragments kept in LDS
+#endif
 #ifndef BWD_DKDV_NSLOT
 #define BWD_DKDV_NSLOT 2
 #endif
