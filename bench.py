@@ -291,8 +291,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the kernels shard by head or batch with no communication; see the design notes)",
+        print("bench.py measures one GPU only: there is no multi-GPU path "
+              "(the kernels would shard by head or batch with no communication)",
               file=sys.stderr)
         sys.exit(2)
 
