@@ -73,8 +73,9 @@ int check_common(int B, int H, int N, int d, int causal, int dtype) {
   return FA_OK;
 }
 
-// Query rows per forward workgroup = 128 * qb.  d = 128 uses 32 rows per wave
-// (register budget); d = 64 uses 64 rows per wave once N is large enough.
+// Query rows per forward workgroup = 128 * qb (32 * qb rows per wave): one
+// block per wave at d = 128 (register budget) and, by default, at d = 64 too
+// (FWD_QB_D64; two blocks at occupancy 2 measured slower than one at 4).
 int fwd_qb(int N, int d) { return d == 128 ? FWD_QB_D128 : (N > 128 ? FWD_QB_D64 : 1); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
