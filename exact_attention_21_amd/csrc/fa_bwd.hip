@@ -484,7 +484,6 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   // step i loads query tile qt0 + i into ring slot SL: Q, dO (swizzled), LSE2, D
   auto issue_step = [&](int i, auto slot) {
-    constexpr int SL = decltype(slot)::value;
     const int qtile = qt0 + i;
     const bool ok = qtile < nqt;
     const uint32_t base = ok ? (uint32_t)qtile * TB : 0x80000000u;

@@ -254,7 +254,6 @@ void fwd_kernel(FwdParams p) {
 
   // S(t) = K(t) Q^T, K(t) in ring slot SL
   auto stage_s = [&](auto slot, f32x16 (&s)[QB]) {
-    constexpr int SL = decltype(slot)::value;
     const char *ks = kslot(slot);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
@@ -344,7 +343,6 @@ void fwd_kernel(FwdParams p) {
   };
   // O^T += V(t)^T P(t)^T, V(t) in ring slot SL
   auto stage_pv = [&](auto slot, const uint32_t (&pk)[QB][8]) {
-    constexpr int SL = decltype(slot)::value;
     const char *vs = vslot(slot);
 #pragma unroll
     for (int c = 0; c < ND32; ++c) {
@@ -379,7 +377,6 @@ void fwd_kernel(FwdParams p) {
 
   // K(t) and V(t) go to ring slot SL
   auto issue_step = [&](int t, auto slot) {
-    constexpr int SL = decltype(slot)::value;
     issue_tile(k_head, t, kslot(slot), dma_k_off);
     issue_tile(v_head, t, vslot(slot), dma_v_off);
   };
