@@ -99,10 +99,24 @@ def _dtype_code(t) -> int:
 
 
 def _check_qkv_like(name, t, ref):
+    """t is a contiguous GPU tensor with ref's device, dtype and shape (checked
+    before any pointer reaches the library: a host pointer handed to a kernel
+    would fault the GPU instead of raising)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
     if t.device != ref.device or t.dtype != ref.dtype or t.shape != ref.shape:
         raise ValueError(f"{name} must match q in device, dtype and shape")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+
+
+def _check_lse(lse, shape, ref):
+    """lse is a contiguous float32 GPU tensor of the given shape on ref's device."""
+    import torch
+    if not lse.is_cuda or lse.device != ref.device:
+        raise ValueError("lse must be a GPU tensor on q's device")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape) or not lse.is_contiguous():
+        raise ValueError(f"lse must be contiguous float32 {list(shape)}")
 
 
 def _stream(stream):
@@ -150,9 +164,7 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         _check_qkv_like(name, t, q)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous() \
-            or lse.device != q.device:
-        raise ValueError("lse must be contiguous float32 [B, H, N] on q's device")
+    _check_lse(lse, (B, H, N), q)
     rc = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                       int(bool(causal)), _dtype_code(q), _stream(stream))
     if rc:
@@ -166,21 +178,17 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool, worksp
     B, H, N, d = q.shape
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _check_qkv_like(name, t, q)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
-    if not workspace.is_contiguous() or workspace.device != q.device:
-        raise ValueError("workspace must be a contiguous device tensor")
-    nbytes = workspace.numel() * workspace.element_size()
+    _check_lse(lse, (B, H, N), q)
     rc = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                       _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
-                      _ptr(workspace), ctypes.c_size_t(nbytes), _stream(stream))
+                      *_ws(workspace, q), _stream(stream))
     if rc:
         raise FaError("fa_bwd", rc)
 
 
 def _ws(workspace, q):
-    if not workspace.is_contiguous() or workspace.device != q.device:
-        raise ValueError("workspace must be a contiguous device tensor")
+    if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous GPU tensor on q's device")
     return _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size())
 
 
@@ -188,11 +196,9 @@ def fa_bwd_preprocess(o, dout, lse, workspace, stream=None) -> None:
     """Stage 1 of fa_bwd: D = rowsum(dO * O) and LSE * log2(e) into the workspace."""
     import torch
     B, H, N, d = o.shape
+    _check_qkv_like("o", o, o)
     _check_qkv_like("dout", dout, o)
-    if not o.is_contiguous():
-        raise ValueError("o must be contiguous [B, H, N, d]")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    _check_lse(lse, (B, H, N), o)
     rc = lib().fa_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(lse), B, H, N, d, _dtype_code(o),
                                  *_ws(workspace, o), _stream(stream))
     if rc:
@@ -230,8 +236,7 @@ def fa_bwd_dq_preprocess(q, k, v, o, dout, lse, dq, scale: float, causal: bool, 
     B, H, N, d = q.shape
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)):
         _check_qkv_like(name, t, q)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    _check_lse(lse, (B, H, N), q)
     rc = lib().fa_bwd_dq_preprocess(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                                     B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
                                     *_ws(workspace, q), _stream(stream))
@@ -266,8 +271,8 @@ def _lens_ptr(lens, B, device):
     import torch
     if lens is None:
         return ctypes.c_void_p(None)
-    if not (isinstance(lens, torch.Tensor) and lens.dtype == torch.int32 and lens.device == device
-            and lens.is_contiguous() and tuple(lens.shape) == (B,)):
+    if not (isinstance(lens, torch.Tensor) and lens.is_cuda and lens.dtype == torch.int32
+            and lens.device == device and lens.is_contiguous() and tuple(lens.shape) == (B,)):
         raise ValueError("sequence lengths must be a contiguous int32 [B] tensor on q's device")
     return _ptr(lens)
 
@@ -277,8 +282,10 @@ def _check_padded(q, k, v):
         raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
     for name, t in (("k", k), ("v", v)):
-        if t.device != q.device or t.dtype != q.dtype or tuple(t.shape) != (B, H, Nk, d):
+        if not t.is_cuda or t.device != q.device or t.dtype != q.dtype or tuple(t.shape) != (B, H, Nk, d):
             raise ValueError(f"{name} must be [B, H, Nk, d] with q's device and dtype")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -294,9 +301,7 @@ def fa_fwd_padded(q, k, v, o, lse, seqlens_q, seqlens_k, scale: float, causal: b
     import torch
     B, H, Nq, Nk, d = _check_padded(q, k, v)
     _check_qkv_like("o", o, q)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() \
-            or lse.device != q.device:
-        raise ValueError("lse must be contiguous float32 [B, H, Nq] on q's device")
+    _check_lse(lse, (B, H, Nq), q)
     rc = lib().fa_fwd_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                              _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_k, B, q.device),
                              B, H, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q),
@@ -314,8 +319,7 @@ def fa_bwd_padded(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, scale
         _check_qkv_like(name, t, q)
     for name, t in (("dk", dk), ("dv", dv)):
         _check_qkv_like(name, t, k)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    _check_lse(lse, (B, H, Nq), q)
     rc = lib().fa_bwd_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                              _ptr(dk), _ptr(dv), _lens_ptr(seqlens_q, B, q.device),
                              _lens_ptr(seqlens_k, B, q.device), B, H, Nq, Nk, d, float(scale),
@@ -360,9 +364,7 @@ def fa_fwd_dropout(q, k, v, o, lse, seqlens_q, seqlens_k, scale: float, causal: 
     import torch
     B, H, Nq, Nk, d = _check_padded(q, k, v)
     _check_qkv_like("o", o, q)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() \
-            or lse.device != q.device:
-        raise ValueError("lse must be contiguous float32 [B, H, Nq] on q's device")
+    _check_lse(lse, (B, H, Nq), q)
     rc = lib().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                               _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_k, B, q.device),
                               B, H, Nq, Nk, d, float(scale), int(bool(causal)), float(dropout_p),
@@ -382,8 +384,7 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, scal
         _check_qkv_like(name, t, q)
     for name, t in (("dk", dk), ("dv", dv)):
         _check_qkv_like(name, t, k)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    _check_lse(lse, (B, H, Nq), q)
     rc = lib().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                               _ptr(dk), _ptr(dv), _lens_ptr(seqlens_q, B, q.device),
                               _lens_ptr(seqlens_k, B, q.device), B, H, Nq, Nk, d, float(scale),
@@ -431,9 +432,7 @@ def fa_fwd_splitkv(q, k, v, o, lse, seqlens_q, seqlens_k, scale: float, causal: 
     import torch
     B, H, Nq, Nk, d = _check_padded(q, k, v)
     _check_qkv_like("o", o, q)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() \
-            or lse.device != q.device:
-        raise ValueError("lse must be contiguous float32 [B, H, Nq] on q's device")
+    _check_lse(lse, (B, H, Nq), q)
     rc = lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                               _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_k, B, q.device),
                               B, H, Nq, Nk, d, float(scale), int(bool(causal)), _dtype_code(q),

@@ -152,7 +152,7 @@ const char *fa_status_str(int s) {
     case FA_ERR_WORKSPACE: return "backward workspace too small";
     case FA_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_ARG: return "scale must be finite and > 0; causal must be 0 or 1; dropout_p in [0, 255.5/256)";
+    case FA_ERR_ARG: return "scale must be finite; causal must be 0 or 1; dropout_p in [0, 255.5/256)";
     default: return "unknown status";
   }
 }
@@ -189,7 +189,7 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, c
   if (rc) return rc;
   rc = check_common(B, H, Nk, d, causal, dtype);
   if (rc) return rc;
-  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
   fa::FwdParams p;
   std::memset(&p, 0, sizeof p);
   if (!dropout_spec(dropout_p, seed, offset, &p.drop)) return FA_ERR_ARG;
@@ -252,7 +252,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
   if (rc) return rc;
   rc = check_common(B, H, Nk, d, causal, dtype);
   if (rc) return rc;
-  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
   const bool decode = Nq == 1;
   const SplitPlan sp = decode ? decode_plan(B, H, Nk, d) : split_plan(B, H, Nq, Nk, d);
   const long long grid = decode ? (long long)B * H * (sp.nsplit / 4) : (long long)sp.n_qtiles * sp.nsplit * B * H;
@@ -325,7 +325,7 @@ int bwd_setup(int B, int H, int Nq, int Nk, const int *lq, const int *lk, int d,
   rc = check_common(B, H, Nq, d, causal, dtype);
   if (rc) return rc;
   if ((long long)(Nq + fa::BWD_DQ_BM - 1) / fa::BWD_DQ_BM * B * H > 0x7fffffffLL) return FA_ERR_SHAPE;
-  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
   if (!workspace) return FA_ERR_NULL;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
   if (!aligned4(lq) || !aligned4(lk)) return FA_ERR_ALIGN;

@@ -305,13 +305,17 @@ void bwd_dq_kernel(BwdParams p) {
     // dropout: dP is masked and scaled (dS = P (Z dP - D), Z = keep * 256 / (256 - p8))
     const u32x4 keep = DROP ? keep_bytes_query_major(qrow, j0, hi, (uint32_t)bh, p.drop.offset, p.drop.k0, p.drop.k1)
                             : u32x4{};
+    // masked tiles: the scores are scaled here and masked to -inf (so the mask
+    // holds for any finite scale, zero and negative included), and the
+    // exponent below multiplies by 1 instead of the scale
     if (need_mask) {  // a separate block: most steps skip it
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        s[r] = key <= lim ? s[r] : -__builtin_inff();
+        s[r] = key <= lim ? s[r] * sl2 : -__builtin_inff();
       }
     }
+    const float mult = need_mask ? 1.f : sl2;
     uint32_t dsk[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -319,7 +323,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * j + e;
-        const float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lse2));  // masked: exp2(-inf) = 0
+        const float pr = fast_exp2(__builtin_fmaf(s[r], mult, -lse2));  // masked: exp2(-inf) = 0
         if constexpr (DROP)
           v2[e] = pr * (kept(keep, r, p.drop.p8) ? __builtin_fmaf(dp[r], p.drop.scale, ndsum) : ndsum);
         else if constexpr (DP_FROM_D)
@@ -563,13 +567,16 @@ void bwd_dkdv_kernel(BwdParams p) {
     // dropout: dV takes P * keep (scaled in the epilogue), dS = P (Z dP - D)
     const u32x4 keep = DROP ? keep_bytes_key_major(key, q0, hi, (uint32_t)bh, p.drop.offset, p.drop.k0, p.drop.k1)
                             : u32x4{};
+    // masked tiles: scaled scores, -inf where masked; the exponent below then
+    // multiplies by 1 instead of the scale (a mask that holds for any finite scale)
     if (need_mask) {  // a separate block: most steps skip it
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qrow = q0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        s[r] = key <= qrow + shift ? s[r] : -__builtin_inff();
+        s[r] = key <= qrow + shift ? s[r] * sl2 : -__builtin_inff();
       }
     }
+    const float mult = need_mask ? 1.f : sl2;
     // in two halves of 16 query rows (register groups 2kb, 2kb + 1): P and dS
     // packed to 16 bits, then dV^T += dO^T P and dK^T += Q^T dS for that half
     // (A operands by transposing reads); each accumulator still adds its kb = 0
@@ -588,7 +595,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rg + e;
           // rows past Lq load LSE2 = D = 0 and Q = dO = 0, so they contribute nothing
-          const float pr = fast_exp2(__builtin_fmaf(s[r], sl2, -lq[e]));  // masked: exp2(-inf) = 0
+          const float pr = fast_exp2(__builtin_fmaf(s[r], mult, -lq[e]));  // masked: exp2(-inf) = 0
           if constexpr (DROP) {
             const bool kp = kept(keep, r, p.drop.p8);
             pv[e] = kp ? pr : 0.f;

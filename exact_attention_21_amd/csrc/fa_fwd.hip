@@ -269,6 +269,9 @@ void fwd_kernel(FwdParams p) {
     const int j0 = t * BN;
     return (CAUSAL && j0 + BN - 1 > wr0 + shift) || (j0 + BN > Lk);
   };
+  // The mask is applied to the scaled scores (scale * log2(e) * s, or -inf),
+  // so that it holds for any finite scale, zero and negative included; the
+  // softmax of a masked tile then multiplies by 1 instead of the scale.
   auto apply_mask = [&](int t, f32x16 (&s)[QB]) {
     const int j0 = t * BN;
 #pragma unroll
@@ -278,20 +281,21 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        s[qb][r] = key <= lim ? s[qb][r] : -__builtin_inff();
+        s[qb][r] = key <= lim ? s[qb][r] * sl2 : -__builtin_inff();
       }
     }
   };
-  // probabilities p = exp2(s * scale * log2(e) - m) of one block against the
-  // reference max m, packed to 16 bits (dropout-masked), and this lane's share
+  // probabilities p = exp2(s * mult - m) of one block against the reference
+  // max m (mult = scale * log2(e), or 1 for a masked tile whose scores are
+  // already scaled), packed to 16 bits (dropout-masked), and this lane's share
   // of the row sum, taken from the unrounded, unmasked values
-  auto probs = [&](const f32x16 &s, float m, uint32_t (&pk)[8], const u32x4 &keep) {
+  auto probs = [&](const f32x16 &s, float mult, float m, uint32_t (&pk)[8], const u32x4 &keep) {
     const float nm = -m;
     float ls = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float e0 = fast_exp2(__builtin_fmaf(s[2 * j], sl2, nm));
-      const float e1 = fast_exp2(__builtin_fmaf(s[2 * j + 1], sl2, nm));
+      const float e0 = fast_exp2(__builtin_fmaf(s[2 * j], mult, nm));
+      const float e1 = fast_exp2(__builtin_fmaf(s[2 * j + 1], mult, nm));
       if constexpr (DROP)  // dropped weights leave P V but not the row sum
         pk[j] = T::pack(kept(keep, 2 * j, p.drop.p8) ? e0 : 0.f, kept(keep, 2 * j + 1, p.drop.p8) ? e1 : 0.f);
       else
@@ -307,13 +311,13 @@ void fwd_kernel(FwdParams p) {
   // running max is still the floor, and NaN fails the test too).  Otherwise,
   // for the whole wave: the lazy update of the running max from the tile's row
   // max, and the probabilities again.
-  auto stage_softmax = [&](f32x16 (&s)[QB], uint32_t (&pk)[QB][8], float (&alpha)[QB],
+  auto stage_softmax = [&](f32x16 (&s)[QB], float mult, uint32_t (&pk)[QB][8], float (&alpha)[QB],
                            const u32x4 (&keep)[QB]) {
     float ls[QB];
     bool over = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      ls[qb] = probs(s[qb], mrun[qb], pk[qb], keep[qb]);
+      ls[qb] = probs(s[qb], mult, mrun[qb], pk[qb], keep[qb]);
       over |= !(ls[qb] <= LAZY_BOUND);
     }
     if (__builtin_amdgcn_ballot_w64(over) == 0) {
@@ -327,17 +331,19 @@ void fwd_kernel(FwdParams p) {
     bool grow_any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(s[qb][0], s[qb][1]);
+      // row max of the scaled scores (the products, so that a negative scale
+      // takes the smallest raw score)
+      float mx = fmaxf(s[qb][0] * mult, s[qb][1] * mult);
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][r], s[qb][r + 1]));
-      mx = max_xhalf(mx) * sl2;
+      for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][r] * mult, s[qb][r + 1] * mult));
+      mx = max_xhalf(mx);
       // per-row lazy update (a lane-wise select, not a branch)
       const bool grow = mx > mrun[qb] + LAZY_TAU;
       const float mu = grow ? mx : mrun[qb];
       alpha[qb] = grow ? fast_exp2(mrun[qb] - mx) : 1.f;
       grow_any |= grow;
       mrun[qb] = mu;
-      lrun[qb] = lrun[qb] * alpha[qb] + probs(s[qb], mu, pk[qb], keep[qb]);
+      lrun[qb] = lrun[qb] * alpha[qb] + probs(s[qb], mult, mu, pk[qb], keep[qb]);
     }
     return grow_any;
   };
@@ -394,9 +400,10 @@ void fwd_kernel(FwdParams p) {
         keep[qb] = keep_bytes_query_major(wr0 + qb * 32 + l32, t * BN, hi, (uint32_t)bh, p.drop.offset,
                                           p.drop.k0, p.drop.k1);
     }
-    if (needs_mask(t)) apply_mask(t, sacc);
+    const bool masked = needs_mask(t);
+    if (masked) apply_mask(t, sacc);
     float alpha[QB];
-    const bool resc = stage_softmax(sacc, pk, alpha, keep);
+    const bool resc = stage_softmax(sacc, masked ? 1.f : sl2, pk, alpha, keep);
     if (__builtin_amdgcn_ballot_w64(resc) != 0) rescale_o(alpha);
     stage_pv(slot, pk);
     wait_vmcnt<(NS - 2) * DMA_PER_STEP>();  // tiles for step t + 1 have landed
@@ -432,8 +439,10 @@ void fwd_kernel(FwdParams p) {
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = lrun[qb] + xhalf(lrun[qb]);
     const int row = wr0 + qb * 32 + l32;
-    // padding rows and rows that see no key: O = 0, LSE = -inf
-    const bool live = row < Lq && lt > 0.f;
+    // padding rows and rows that see no key (row sum exactly 0): O = 0,
+    // LSE = -inf; a live row's sum is >= 1 (its largest term is taken against
+    // a running max no larger than the row's max), and NaN stays NaN
+    const bool live = row < Lq && lt != 0.f;
     const float inv = (DROP ? p.drop.scale : 1.f) / lt;  // kept weights are scaled by 256 / (256 - p8)
     if (SPLIT && row < Nq) {
 #pragma unroll
@@ -487,10 +496,11 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float *__restric
   if (row >= rows) return;  // whole waves exit together
   const long bh = row / Nq, i = row % Nq;
   const float *ls = lpart + (size_t)bh * nsplit * Nq + i;  // stride Nq between chunks
+  // NaN-propagating maximum: a NaN partial makes the row NaN
   float m = -__builtin_inff();
-  for (int s = lane; s < nsplit; s += 64) m = fmaxf(m, ls[(size_t)s * Nq]);
+  for (int s = lane; s < nsplit; s += 64) m = __builtin_elementwise_maximum(m, ls[(size_t)s * Nq]);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  for (int off = 32; off > 0; off >>= 1) m = __builtin_elementwise_maximum(m, __shfl_xor(m, off, 64));
   float acc[CPL] = {};
   float wsum = 0.f;
   if (m != -__builtin_inff()) {
@@ -502,7 +512,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float *__restric
       for (int c = 0; c < CPL; ++c) acc[c] += w * os[c];
     }
   }
-  const bool live = wsum > 0.f;
+  const bool live = wsum != 0.f;  // no visible key: 0; NaN stays NaN
   uint16_t *orow = o + (size_t)row * D + lane * CPL;
   if constexpr (CPL == 2) {
     *reinterpret_cast<uint32_t *>(orow) = live ? T::pack(acc[0] / wsum, acc[1] / wsum) : 0u;
@@ -575,11 +585,11 @@ __global__ __launch_bounds__(256) void fwd_decode_kernel(FwdParams p) {
       dt = T::dot2(kv[i][3], qv[3], dt);
       dt = group_sum<LPK>(dt);
       s[i] = t0 + i * KPL + g < j1 ? dt * sl2 : -__builtin_inff();
-      mt = fmaxf(mt, s[i]);
+      mt = __builtin_elementwise_maximum(mt, s[i]);  // NaN-propagating (v_maximum3_f32)
     }
 #pragma unroll
-    for (int off = LPK; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off, 64));
-    const float mn = fmaxf(m, mt);
+    for (int off = LPK; off < 64; off <<= 1) mt = __builtin_elementwise_maximum(mt, __shfl_xor(mt, off, 64));
+    const float mn = __builtin_elementwise_maximum(m, mt);
     if (mn == -__builtin_inff()) continue;  // wave-uniform: no visible key yet
     const float alpha = fast_exp2(m - mn);  // 0 while m = -inf
     m = mn;
@@ -605,7 +615,7 @@ __global__ __launch_bounds__(256) void fwd_decode_kernel(FwdParams p) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] += __shfl_xor(o[c], off, 64);
   }
-  const bool live = l > 0.f;
+  const bool live = l != 0.f;  // no visible key: 0; NaN stays NaN
   const size_t prow = (size_t)bh * p.nsplit + split;  // Nq = 1
   if (g == 0) {
     const float inv = live ? 1.f / l : 0.f;

@@ -25,7 +25,10 @@
  *     recommended configuration: FP16/BF16 only), accumulation is fp32.
  *   - head_dim d must be 64 or 128.  Any N >= 1 is accepted; ragged tails are
  *     masked inside the kernels.
- *   - scale must be finite and > 0 (the pages use 1/sqrt(d_k)).
+ *   - scale is any finite float (the pages use 1/sqrt(d_k) for it; 0 gives the
+ *     plain mean of the visible V rows, a negative scale favours the smallest
+ *     scores).  The mask is applied to the scaled scores, so it holds for every
+ *     finite scale.
  *   - causal = 1 applies the lower-triangular mask of a square attention
  *     matrix: query i sees key j iff j <= i (handbook ch.3, notes on the causal
  *     mask: future positions are skipped); fully masked tiles are never loaded.
@@ -59,7 +62,7 @@ typedef enum {
   FA_ERR_WORKSPACE = 6, /* backward workspace too small */
   FA_ERR_DEVICE = 7,    /* current device is not gfx950, or no device */
   FA_ERR_LAUNCH = 8,    /* the HIP runtime rejected a kernel launch */
-  FA_ERR_ARG = 9        /* scale not finite and positive, causal not 0/1, or dropout_p out of range */
+  FA_ERR_ARG = 9        /* scale not finite, causal not 0/1, or dropout_p out of range */
 } fa_status_t;
 
 /*

@@ -76,10 +76,13 @@ def test_forward_validation_order_without_gpu():
     assert _fwd_raw(N=0) == 2                       # shape
     assert _fwd_raw(d=80) == 3                      # head dim
     assert _fwd_raw(dtype=7) == 4                   # dtype
-    assert _fwd_raw(scale=0.0) == 9                 # scale must be > 0
-    assert _fwd_raw(scale=float("nan")) == 9
-    assert _fwd_raw(scale=-1.0) == 9
+    assert _fwd_raw(scale=float("nan")) == 9       # scale must be finite
+    assert _fwd_raw(scale=float("inf")) == 9
+    assert _fwd_raw(scale=float("-inf")) == 9
     assert _fwd_raw(ptr=24) == 5                    # misaligned
+    # zero and negative scales are valid arguments: they pass to the later checks
+    assert _fwd_raw(ptr=24, scale=0.0) == 5
+    assert _fwd_raw(ptr=24, scale=-1.0) == 5
     # valid arguments: the device gate is the only thing left
     import torch
     if not torch.cuda.is_available():
@@ -93,7 +96,9 @@ def test_backward_validation_without_gpu():
     need = fa.fa_bwd_workspace_size(1, 1, 16, 64)
     assert lib.fa_bwd(*args, None, need, None) == 1
     assert lib.fa_bwd(*args, p, need - 1, None) == 6
-    assert lib.fa_bwd(*([p] * 9 + [1, 1, 16, 128, -0.5, 0, 0]), p, 10 ** 9, None) == 9
+    assert lib.fa_bwd(*([p] * 9 + [1, 1, 16, 128, float("nan"), 0, 0]), p, 10 ** 9, None) == 9
+    # a negative scale is valid: the call gets as far as the workspace check
+    assert lib.fa_bwd(*([p] * 9 + [1, 1, 16, 128, -0.5, 0, 0]), p, 1, None) == 6
     assert lib.fa_bwd(*([ctypes.c_void_p(72)] + [p] * 8 + [1, 1, 16, 64, 0.125, 0, 0]), p, need, None) == 5
 
 

@@ -77,6 +77,43 @@ def test_identical_keys_give_mean_of_values(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_gives_mean_of_visible_values(causal):
+    # scale = 0: every visible score is 0, so the weights are uniform over the
+    # visible keys: O_i = mean of V over them (prefix means when causal),
+    # LSE_i = ln n_i; dQ = dK = 0 (both carry the factor scale) and
+    # dV_j = sum over the rows i that see key j of dO_i / n_i
+    B, H, N, d = 2, 2, 11, 8
+    q, k, v, do = (rnd((B, H, N, d), 300 + i, 3.0) for i in range(4))
+    o, lse = oracle.fwd(q, k, v, 0.0, causal)
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.0, causal)
+    n = np.arange(1, N + 1) if causal else np.full(N, N)
+    for i in range(N):
+        np.testing.assert_allclose(o[:, :, i], v[:, :, :n[i]].mean(axis=2), atol=1e-12)
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(n), lse.shape), atol=1e-14)
+    assert not dq.any() and not dk.any()
+    for j in range(N):
+        rows = [i for i in range(N) if (i >= j or not causal)]
+        want = sum(do[:, :, i] / n[i] for i in rows)
+        np.testing.assert_allclose(dv[:, :, j], want, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_negative_scale_equals_negated_keys(causal):
+    # softmax(-s q.k) = softmax(s q.(-k)): the forward at -s on K equals the
+    # forward at s on -K; by the chain rule dQ and dV agree and dK changes sign
+    q, k, v, do = (rnd((1, 2, 9, 6), 310 + i) for i in range(4))
+    o1, l1 = oracle.fwd(q, k, v, -0.45, causal)
+    o2, l2 = oracle.fwd(q, -k, v, 0.45, causal)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+    g1 = oracle.bwd(q, k, v, do, -0.45, causal)
+    g2 = oracle.bwd(q, -k, v, do, 0.45, causal)
+    np.testing.assert_allclose(g1[0], g2[0], atol=1e-13)
+    np.testing.assert_allclose(g1[1], -g2[1], atol=1e-13)
+    np.testing.assert_allclose(g1[2], g2[2], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_single_key_returns_v_exactly(causal):
     q, k, v = rnd((2, 3, 1, 16), 4), rnd((2, 3, 1, 16), 5), rnd((2, 3, 1, 16), 6)
     o, lse = oracle.fwd(q, k, v, 0.25, causal)
@@ -109,10 +146,12 @@ def test_probability_rows_sum_to_one(causal):
 @pytest.mark.parametrize("N", [1, 2, 3, 5, 8])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("mag", [1.0, 12.0])
-def test_lse_and_output_match_50_digit_brute_force(N, causal, mag):
+@pytest.mark.parametrize("scale", [0.5, -0.8, 0.0])
+def test_lse_and_output_match_50_digit_brute_force(N, causal, mag, scale):
+    # the scale is a free argument of the formula: the usual 1/sqrt(d) (d = 4),
+    # a negative one (the smallest raw scores get the largest weights) and 0
     d = 4
     q, k, v = rnd((1, 1, N, d), 20 + N, mag), rnd((1, 1, N, d), 30 + N, mag), rnd((1, 1, N, d), 40 + N)
-    scale = 1 / math.sqrt(d)
     o, lse = oracle.fwd(q, k, v, scale, causal)
     mpmath.mp.dps = 50
     for i in range(N):
@@ -224,10 +263,10 @@ def torch_reference(q, k, v, dout, scale, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_matches_torch_fp64_autograd(causal):
+@pytest.mark.parametrize("scale", [0.25, -0.7, 0.0])
+def test_matches_torch_fp64_autograd(causal, scale):
     shape = (2, 3, 40, 16)
     q, k, v, do = (rnd(shape, 90 + i) for i in range(4))
-    scale = 1 / math.sqrt(16)
     o, lse = oracle.fwd(q, k, v, scale, causal)
     dq, dk, dv = oracle.bwd(q, k, v, do, scale, causal)
     to, tl, tdq, tdk, tdv = torch_reference(q, k, v, do, scale, causal)

@@ -42,7 +42,10 @@ PINS = [
     lambda: pins.test_identical_keys_give_mean_of_values(True),
     lambda: pins.test_causal_row0_is_v0(),
     lambda: pins.test_probability_rows_sum_to_one(True),
-    lambda: pins.test_lse_and_output_match_50_digit_brute_force(5, True, 12.0),
+    lambda: pins.test_lse_and_output_match_50_digit_brute_force(5, True, 12.0, 0.5),
+    lambda: pins.test_lse_and_output_match_50_digit_brute_force(5, True, 1.0, -0.8),
+    lambda: pins.test_zero_scale_gives_mean_of_visible_values(True),
+    lambda: pins.test_negative_scale_equals_negated_keys(True),
     lambda: pins.test_huge_scores_stay_finite(),
     lambda: pins.test_backward_central_differences(True, 5, 4),
     lambda: pins.test_backward_invariants(True),

@@ -7,13 +7,21 @@ the other parity tests: O max-abs <= 2e-2 (bf16) / 4e-3 (fp16), LSE <= 1e-3,
 gradients max-abs <= 5e-2 and rel-Frobenius <= 1e-2; rows that see no key are
 exactly O = 0, LSE = -inf.
 
-The rel-Frobenius bar is applied when at least 16 query rows are live.  With
-fewer, one row can carry the whole norm, and a row whose weight sits on one
-key (P = 0.92, 0.05, 0.02 over 3 keys, say) has dS = P (dP - D) made of
-near-cancelling terms: the backward takes D from the 16-bit O it is given,
-and that rounding alone moves the fp64 reference dQ of such a row by 1.0e-2
-relative (computed for random case 63 with the oracle's own O rounded to
-bf16).  Max-abs is checked in every case."""
+The rel-Frobenius bar of dQ and dK is widened by a bound computed per case:
+the backward forms D = rowsum(dO * O) from the 16-bit O it is given, and with
+few live rows one row can carry the whole norm of a gradient; a row whose
+weight sits on one key (P = 0.92, 0.05, 0.02 over 3 keys, say) has
+dS = P (dP - D) made of near-cancelling terms, so the rounding of O alone
+moves its fp64 reference gradient by ~1e-2 relative.  The gradients are affine
+in D (dS changes by -P dD, with no dropout factor), so that change is exact:
+with dD = rowsum(dO * (round(O) - O)) from the oracle's own O,
+  delta dQ = -scale dD (P K)   and   delta dK = -scale P^T (dD * Q),
+where P K is the oracle's forward with V = K and P^T X the oracle's dV for the
+upstream gradient X.  dQ and dK must be within 1e-2 + 2 |delta| / |ref|
+(twice: the O the GPU hands its backward is within about one unit in the last
+place of the exact O, the rounding within half of one); dV does not involve D
+and always has the plain 1e-2 bar.  Max-abs is checked in every case.
+"""
 import math
 
 import numpy as np
@@ -86,10 +94,27 @@ def test_random_shape(gpu, i):
         check_fwd(to_host_f64(split[0]), to_host_f64(split[1]), ro, rl, dtype, "split forward")
     ref = oracle.bwd_padded(*w, scale, causal, lq, lk, dropout=drop)
     live_rows = int(np.isfinite(rl).sum())
+    sens = d_rounding_sensitivity(w, ro, ref, scale, causal, lq, lk, dtype)
     for name, got, want in zip(("dQ", "dK", "dV"), grads, ref):
         g = to_host_f64(got)
         ea, er = max_abs(g, want), rel_frob(g, want)
-        say(f"    {name}: max-abs {ea:.3e} rel-F {er:.3e} ({live_rows} live rows)")
+        bar = TOL_GRAD_RELF + 2.0 * sens.get(name, 0.0)
+        say(f"    {name}: max-abs {ea:.3e} rel-F {er:.3e} (bar {bar:.3e}; {live_rows} live rows)")
         assert ea <= TOL_GRAD_ABS, (name, ea)
-        if live_rows >= 16:
-            assert er <= TOL_GRAD_RELF, (name, er)
+        assert er <= bar, (name, er, bar)
+
+
+def d_rounding_sensitivity(w, ro, ref, scale, causal, lq, lk, dtype):
+    """Relative change of the oracle's dQ and dK when D is formed from its own O
+    rounded to the storage dtype (exact: the gradients are affine in D)."""
+    q, k, v, do = w
+    o16 = fa_inputs.widen(fa_inputs.narrow(ro, dtype), dtype)
+    dD = np.sum(do * (o16 - ro), axis=-1)                      # [B, H, Nq]
+    pk, _ = oracle.fwd_padded(q, k, k, scale, causal, lq, lk)  # P K
+    delta_dq = -scale * dD[..., None] * pk
+    delta_dk = -scale * oracle.bwd_padded(q, k, v, dD[..., None] * q, scale, causal, lq, lk)[2]  # P^T (dD Q)
+    out = {}
+    for name, delta, want in (("dQ", delta_dq, ref[0]), ("dK", delta_dk, ref[1])):
+        den = float(np.linalg.norm(want))
+        out[name] = float(np.linalg.norm(delta)) / den if den > 0 else 0.0
+    return out
