@@ -7,7 +7,7 @@ the library's kernels.  There is no fallback: if libfa.so is missing or the
 device is not gfx950 the calls raise.
 
 Names mirror the C ABI: fa_fwd, fa_bwd (and its stages fa_bwd_preprocess,
-fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dq_preprocess), fa_fwd_padded, fa_bwd_padded, fa_fwd_dropout,
+fa_bwd_dkdv, fa_bwd_dq, fa_bwd_dq_preprocess), fa_bwd_noalloc, fa_fwd_padded, fa_bwd_padded, fa_fwd_dropout,
 fa_bwd_dropout, fa_fwd_splitkv, fa_fwd_splitkv_workspace_size,
 fa_bwd_workspace_size, fa_fwd_plan, fa_bwd_plan, fa_status_str.
 fwd(), bwd(), fwd_padded(), bwd_padded(), fwd_dropout(), bwd_dropout() and
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_dq_preprocess.restype = I
         L.fa_fwd_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, I, vp]
         L.fa_fwd_padded.restype = I
+        L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, F, I, I, vp]
+        L.fa_bwd_noalloc.restype = I
         L.fa_bwd_padded.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, F, I, I,
                                     vp, Z, vp]
         L.fa_bwd_padded.restype = I
@@ -184,6 +186,26 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool, worksp
                       *_ws(workspace, q), _stream(stream))
     if rc:
         raise FaError("fa_bwd", rc)
+
+
+FA_BWD_NOALLOC_MAX_ROWS = 4194304  # include/fa.h
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, scale: float, causal: bool,
+                   stream=None) -> None:
+    """fa_bwd without a workspace: the row statistics live in the library's static
+    per-GPU scratch (B*H*N <= FA_BWD_NOALLOC_MAX_ROWS).  Allocates nothing; calls
+    that overlap on one GPU race (see include/fa.h)."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _check_qkv_like(name, t, q)
+    _check_lse(lse, (B, H, N), q)
+    rc = lib().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                              _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                              _dtype_code(q), _stream(stream))
+    if rc:
+        raise FaError("fa_bwd_noalloc", rc)
 
 
 def _ws(workspace, q):

@@ -1,9 +1,11 @@
 // C-ABI layer: argument validation, launch planning, device gating and kernel
-// launches for the fused attention library.  No allocation, no global mutable
-// state apart from a per-device "is gfx950" cache.
+// launches for the fused attention library.  No allocation; global mutable
+// state is limited to per-device caches (the "is gfx950" check and the device
+// address of the no-allocation backward's static scratch array).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -12,6 +14,15 @@
 
 #include "fa.h"
 #include "fa_kernels.h"
+
+// Scratch of fa_bwd_noalloc: the backward workspace (-D and LSE * log2(e), fp32,
+// one 256-byte aligned block each) for up to FA_BWD_NOALLOC_MAX_ROWS query
+// rows.  Each GPU the library runs on holds its own copy until the process
+// ends.  In host code `scratch` is only a handle for the runtime: its device
+// address (per device) comes from hipGetSymbolAddress, and only that address
+// is ever handed to a kernel.
+constexpr size_t kScratchBytes = 2 * (size_t)FA_BWD_NOALLOC_MAX_ROWS * sizeof(float);
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -31,6 +42,27 @@ int check_device() {
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? FA_OK : FA_ERR_DEVICE;
+}
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device `dev` (which must be current), looked
+// up once per device; nullptr if the runtime cannot resolve it.
+void *scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -153,6 +185,7 @@ const char *fa_status_str(int s) {
     case FA_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ARG: return "scale must be finite; causal must be 0 or 1; dropout_p in [0, 255.5/256)";
+    case FA_ERR_SCRATCH: return "fa_bwd_noalloc: B*H*N exceeds FA_BWD_NOALLOC_MAX_ROWS (4194304 rows)";
     default: return "unknown status";
   }
 }
@@ -491,6 +524,25 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            void *stream) {
   return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, H, N, N, d, scale, causal,
                   0.f, 0, 0, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                   const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+                   float scale, int causal, int dtype, void *stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  int rc = check_common(B, H, N, d, causal, dtype);
+  if (rc) return rc;
+  if ((long double)B * H * N > (long double)FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d);
+  if (need == 0 || need > kScratchBytes) return FA_ERR_SCRATCH;
+  rc = check_device();
+  if (rc) return rc;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_DEVICE;
+  void *ws = scratch_ptr(dev);
+  if (!ws) return FA_ERR_DEVICE;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, H, N, N, d, scale, causal,
+                  0.f, 0, 0, dtype, ws, kScratchBytes, stream);
 }
 
 int fa_bwd_padded(const void *q, const void *k, const void *v, const void *o, const void *dout,

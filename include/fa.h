@@ -62,7 +62,8 @@ typedef enum {
   FA_ERR_WORKSPACE = 6, /* backward workspace too small */
   FA_ERR_DEVICE = 7,    /* current device is not gfx950, or no device */
   FA_ERR_LAUNCH = 8,    /* the HIP runtime rejected a kernel launch */
-  FA_ERR_ARG = 9        /* scale not finite, causal not 0/1, or dropout_p out of range */
+  FA_ERR_ARG = 9,       /* scale not finite, causal not 0/1, or dropout_p out of range */
+  FA_ERR_SCRATCH = 10   /* fa_bwd_noalloc: B*H*N exceeds FA_BWD_NOALLOC_MAX_ROWS */
 } fa_status_t;
 
 /*
@@ -98,6 +99,28 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            const void *dout, const float *lse, void *dq, void *dk, void *dv,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, the same kernels and bitwise the same
+ * results as fa_bwd.  The backward's row statistics (-D and LSE * log2(e),
+ * 8 bytes per query row) live in a static device array of the library, one per
+ * GPU, held until the process ends; the call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).  The array's device address is
+ * looked up once per device, on the first call with that device current.
+ * Limit: B*H*N <= FA_BWD_NOALLOC_MAX_ROWS (32 MiB of scratch), else
+ * FA_ERR_SCRATCH.  Nothing in the array needs to start at zero: each call
+ * writes every row statistic before reading it.  All calls on one GPU share
+ * the array, so calls that overlap on one GPU (concurrent streams, threads, or
+ * a captured graph replayed concurrently with another call) race and give
+ * wrong results; calls on different GPUs are independent.
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS 4194304
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                   const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                   int B, int H, int N, int d, float scale, int causal, int dtype,
+                   void *stream);
 
 /*
  * The stages of the backward, exposed so that a caller can schedule or time

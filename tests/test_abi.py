@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(11):
         assert fa.fa_status_str(s) and fa.fa_status_str(s) != "unknown status"
     assert fa.fa_status_str(99) == "unknown status"
 
@@ -133,3 +133,21 @@ def test_split_workspace_covers_every_chunk():
         assert ws >= B * H * Nq * d * 4 + B * H * Nq * 4  # at least one chunk
         assert ws % 256 == 0
     assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1, 16, 96) == 0  # unsupported head size
+
+
+def test_noalloc_limits_without_gpu():
+    lib = fa.lib()
+    p = ctypes.c_void_p(64)
+    rows = fa.FA_BWD_NOALLOC_MAX_ROWS
+    assert re.search(r"#define FA_BWD_NOALLOC_MAX_ROWS %d\b" % rows, open(HEADER).read())
+    args = lambda B, H, N, d=64: [p] * 9 + [B, H, N, d, ctypes.c_float(0.125), 0, 0, None]
+    assert lib.fa_bwd_noalloc(*([None] + [p] * 8 + args(1, 1, 16)[9:])) == 1   # null
+    assert lib.fa_bwd_noalloc(*args(1, 1, 16, 80)) == 3                          # head dim
+    assert lib.fa_bwd_noalloc(*args(1, 1, rows + 1)) == 10                       # beyond the scratch
+    assert lib.fa_bwd_noalloc(*args(4, 32, 32768 + 1)) == 10
+    # at the limit the argument checks pass: the device gate is what remains
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.fa_bwd_noalloc(*args(4, 32, rows // 128)) == 7
+        assert lib.fa_bwd_noalloc(*args(1, 1, rows)) == 7
+
