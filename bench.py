@@ -11,9 +11,12 @@ FLOP convention: 4*B*H*N^2*d for the forward, halved when causal; the backward
 counts 2.5x the forward.  `value` is (forward + backward FLOP) / step time.
 
 Per-kernel figures are measured live with HIP events recorded on the stream the
-kernels run on.  The CPU baseline times the fp64 oracle on a bounded sample of
-the same workload (one head: the forward over every row, the backward over the
-whole head) on the host's cores.
+kernels run on (mean, median and minimum over the timed steps; FLOP rates as
+executed work and as the method's share of the work).  The CPU baseline times
+the fp64 oracle on bounded samples on the host's cores: one head of this
+workload (the forward over 2048 rows spread over it and the backward of the
+whole head), and per configuration of the family a forward row sample (and the
+4096 backward configuration's backward of one head).
 
 After the headline step the other configurations of the workload family (the
 sequence-length sweep N = 1k..32k at 32768 tokens per batch, the d=64 variant,
@@ -30,6 +33,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -101,31 +105,99 @@ def make_inputs(w, device):
     return bits, tens
 
 
-def cpu_baseline(bits, w, max_bwd_n):
-    """fp64 oracle on one head of the workload: forward over all rows, backward over the head."""
+def cpu_info():
+    """CPU model, logical CPUs and the CPUs this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def _timed(fn, reps):
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return ts
+
+
+def _stats(ts, flop):
+    med = statistics.median(ts)
+    return {"median_s": med, "min_s": min(ts), "mean_s": sum(ts) / len(ts), "runs": len(ts),
+            "flop": flop, "tflops_median": flop / med / 1e12, "tflops_best": flop / min(ts) / 1e12}
+
+
+def cpu_baseline(bits, w, max_bwd_n, fwd_rows=2048, reps=3):
+    """The fp64 oracle, as it is, on bounded samples of the workloads, on the
+    host's cores (its default thread count).
+
+    Headline (the bench workload, one head of it): the forward over `fwd_rows`
+    rows spread evenly over head (0,0) plus the backward of that whole head;
+    value = their nominal FLOP / time (4 d FLOP per visible (query, key) pair
+    forward, 2.5x that backward).  Per configuration of the family: the
+    forward over the same kind of row sample of head (0,0) (median, minimum and
+    mean of `reps` runs), and for the backward configuration also the
+    backward of head (0,0).  Inputs are the seeded draws of each workload."""
     import numpy as np
     import fa_inputs
     import oracle
     threads = oracle.default_threads()
+    info = cpu_info()
+
+    def fwd_sample(q, k, v, N, d, causal):
+        rows = np.unique(np.linspace(0, N - 1, min(N, fwd_rows)).round().astype(np.int64))
+        vis = (rows + 1) if causal else np.full(len(rows), N)
+        return rows, 4.0 * d * float(vis.sum())
+
+    # headline: the bench workload's head (0,0)
     N, d, causal = w["N"], w["d"], w["causal"]
     scale = float(np.float32(1 / math.sqrt(d)))
     sub = [fa_inputs.widen(x[0:1, 0:1], w["dtype"]) for x in bits]
-    rows = np.arange(N)
-    t0 = time.perf_counter()
-    oracle.fwd_rows(*sub[:3], scale, causal, rows, threads=threads)
-    t_fwd = time.perf_counter() - t0
-    f_fwd, f_bwd = nominal_flop(1, 1, N, d, causal)
-    flop, secs = f_fwd, t_fwd
-    sample = f"head (0,0): forward over all {N} rows"
+    rows, f_rows = fwd_sample(*sub[:3], N, d, causal)
+    t_fwd = _timed(lambda: oracle.fwd_rows(*sub[:3], scale, causal, rows, threads=threads), reps)
+    flop, secs = f_rows, statistics.median(t_fwd)
+    sample = f"head (0,0) of {w['name']}: forward over {len(rows)} rows spread over the head ({secs:.2f} s median of {reps})"
+    head = {"fwd": _stats(t_fwd, f_rows)}
     if N <= max_bwd_n:
-        t0 = time.perf_counter()
-        oracle.bwd_heads(*sub, scale, causal, [0], threads=threads)
-        t_bwd = time.perf_counter() - t0
+        _, f_bwd = nominal_flop(1, 1, N, d, causal)
+        t_bwd = _timed(lambda: oracle.bwd_heads(*sub, scale, causal, [0], threads=threads), 1)
+        head["bwd"] = _stats(t_bwd, f_bwd)
         flop += f_bwd
-        secs += t_bwd
-        sample += f" ({t_fwd:.1f} s) + backward of the whole head ({t_bwd:.1f} s)"
+        secs += t_bwd[0]
+        sample += f" + backward of the whole head ({t_bwd[0]:.1f} s)"
+    per = {w["name"]: head}
+    # the other configurations of the family (forward samples; the backward
+    # configuration also with its backward)
+    for name, c in fa_inputs.CONFIGS.items():
+        if name.startswith("c3_") or not name.startswith(("c1_", "c2_", "c4_", "c5_")):
+            continue
+        B, H, Nc, dc, cc = c["B"], c["H"], c["N"], c["d"], c["causal"]
+        xb = fa_inputs.qkv_bits(1, 1, Nc, dc, c["dtype"], c["seed"], with_dout=c.get("bwd", False))
+        xs = [fa_inputs.widen(x, c["dtype"]) for x in xb]
+        sc = float(np.float32(1 / math.sqrt(dc)))
+        r, f = fwd_sample(*xs[:3], Nc, dc, cc)
+        entry = {"fwd": _stats(_timed(lambda: oracle.fwd_rows(*xs[:3], sc, cc, r, threads=threads), reps), f),
+                 "rows": int(len(r)), "N": Nc, "d": dc, "causal": cc}
+        if c.get("bwd"):
+            _, fb = nominal_flop(1, 1, Nc, dc, cc)
+            entry["bwd"] = _stats(_timed(lambda: oracle.bwd_heads(*xs, sc, cc, [0], threads=threads), 1), fb)
+        per[name] = entry
+        log(f"[bench] cpu baseline {name}: fwd {entry['fwd']['tflops_median'] * 1e3:.2f} GFLOP/s"
+            + (f", bwd {entry['bwd']['tflops_median'] * 1e3:.2f} GFLOP/s" if "bwd" in entry else ""))
     return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": sample + f"; nominal FLOP {flop:.3e} in {secs:.1f} s"}
+            "sample": sample + f"; nominal FLOP {flop:.3e} in {secs:.1f} s",
+            "threads": threads, **info, "per_config": per}
 
 
 def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
@@ -348,37 +420,52 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    def times_ms(i, j):
+        return [e[i].elapsed_time(e[j]) for e in evs]
+
     def avg_ms(i, j):
-        return sum(e[i].elapsed_time(e[j]) for e in evs) / len(evs)
+        t = times_ms(i, j)
+        return sum(t) / len(t)
 
     f_fwd, f_bwd = nominal_flop(B, H, N, d, causal)
     ms_step = wall * 1e3 / args.steps
-    kern = {"fwd_kernel": (avg_ms(0, 1), f_fwd)}
+    # per kernel: event times and two FLOP counts.  Every tile product is
+    # 2 B H N^2 d (halved when causal), half the nominal forward.  "executed":
+    # the products the kernel runs; "method": its share of the method's work
+    # (forward 2 products, backward 5: S and dP recomputed, dV, dK, dQ).  The
+    # dK/dV pass runs four (S, dP, dV, dK), all method work; the dQ pass runs
+    # three (S, dP, dQ) of which only dQ is not also done by the dK/dV pass.
+    half = 0.5 * f_fwd
+    kern = {"fwd_kernel": ((0, 1), 2 * half, 2 * half)}
     if not args.fwd_only:
-        # algorithmic FLOP of each backward pass: dK/dV runs 4 of the tile
-        # products (S, dP, dV, dK), dQ runs 3 (S, dP, dQ); each is 2 B H N^2 d
-        # (halved when causal), i.e. half the nominal forward's 4 B H N^2 d
-        kern["bwd_dq_kernel"] = (avg_ms(1, 2), 1.5 * f_fwd)
-        kern["bwd_dkdv_kernel"] = (avg_ms(2, 3), 2.0 * f_fwd)
-    fwd_avg = kern["fwd_kernel"][0]
+        kern["bwd_dq_kernel"] = ((1, 2), 3 * half, 1 * half)
+        kern["bwd_dkdv_kernel"] = ((2, 3), 4 * half, 4 * half)
+    fwd_avg = avg_ms(0, 1)
     bwd_avg = avg_ms(1, 3) if not args.fwd_only else 0.0
     total_flop = f_fwd + (0 if args.fwd_only else f_bwd)
     fwd_tf = f_fwd / (fwd_avg * 1e-3) / 1e12
     bwd_tf = f_bwd / (bwd_avg * 1e-3) / 1e12 if not args.fwd_only else None
-    for name, (ms, fl) in kern.items():
-        log(f"[bench] {name}: {ms:.3f} ms" + (f" ({fl / (ms * 1e-3) / 1e12:.0f} TFLOP/s)" if fl else ""))
+    kernels = {}
+    for name, ((i, j), f_exec, f_meth) in kern.items():
+        t = times_ms(i, j)
+        ms = sum(t) / len(t)
+        kernels[name] = {"avg_ms": ms, "median_ms": statistics.median(t), "min_ms": min(t),
+                         "executed_flop": f_exec, "method_flop": f_meth,
+                         "executed_tflops": f_exec / (ms * 1e-3) / 1e12,
+                         "method_tflops": f_meth / (ms * 1e-3) / 1e12,
+                         "method_frac_of_peak": f_meth / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        log(f"[bench] {name}: {ms:.3f} ms (median {statistics.median(t):.3f}, min {min(t):.3f}); "
+            f"executed {kernels[name]['executed_tflops']:.0f} TFLOP/s, method {kernels[name]['method_tflops']:.0f}")
     log(f"[bench] fwd {fwd_avg:.3f} ms ({fwd_tf:.0f} TFLOP/s)"
         + ("" if args.fwd_only else f"  bwd {bwd_avg:.3f} ms ({bwd_tf:.0f} TFLOP/s nominal)"))
 
-    dom = max(kern, key=lambda n: kern[n][0])
-    dom_ms, dom_flop = kern[dom]
+    # the roofline entry is for the longest kernel (method work = executed work there)
+    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"])
+    dom_ms, dom_flop = kernels[dom]["avg_ms"], kernels[dom]["method_flop"]
     dom_tf = dom_flop / (dom_ms * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": dom_tf, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": dom_tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
                 "avg_launch_ms": dom_ms, "algorithmic_flop_per_launch": dom_flop}
-    kernels = {n: {"avg_ms": ms, "tflops": (fl / (ms * 1e-3) / 1e12) if fl else None,
-                   "frac_of_peak": (fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS) if fl else None}
-               for n, (ms, fl) in kern.items()}
 
     swp = None
     if not args.no_sweep and not args.fwd_only:
@@ -407,6 +494,9 @@ def main():
                    "B": B, "H": H, "N": N, "d": d, "causal": causal, "pass": "fwd+bwd" if not args.fwd_only else "fwd",
                    "flop_per_step": total_flop},
         "fwd_ms": fwd_avg, "bwd_ms": bwd_avg if not args.fwd_only else None,
+        "fwd_ms_median": statistics.median(times_ms(0, 1)), "fwd_ms_min": min(times_ms(0, 1)),
+        "bwd_ms_median": statistics.median(times_ms(1, 3)) if not args.fwd_only else None,
+        "bwd_ms_min": min(times_ms(1, 3)) if not args.fwd_only else None,
         "fwd_tflops": fwd_tf, "bwd_tflops": bwd_tf,
         "fwd_frac_of_peak": fwd_tf / PEAK_BF16_TFLOPS,
         "bwd_frac_of_peak": (bwd_tf / PEAK_BF16_TFLOPS) if bwd_tf else None,

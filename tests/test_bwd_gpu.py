@@ -143,3 +143,43 @@ def test_workspace_too_small_is_rejected(gpu):
     with pytest.raises(fa.FaError) as e:
         fa.fa_bwd(q, q, q, q, q, lse, q.clone(), q.clone(), q.clone(), 0.125, False, ws)
     assert e.value.status == 6
+
+
+@pytest.mark.parametrize("B,H", [(32, 8), (21, 13)], ids=["xcd_grouped", "not_grouped"])
+def test_large_grid_covers_every_block(gpu, B, H):
+    # Many heads of short sequences: 2048+ key blocks of the dK/dV pass and as
+    # many query blocks of the dQ pass, heads grouped per XCD (B*H a multiple
+    # of 8) or not.  Outputs are pre-filled with NaN, so a block that no
+    # workgroup wrote would show; two calls in a row give the same bits.
+    import torch
+    N, d, dtype = 1024, 128, "bf16"
+    say(f"[bwd large grid] B={B} H={H} N={N}")
+    qb, kb, vb, dob = fa_inputs.qkv_bits(B, H, N, d, dtype, seed=2300 + H, with_dout=True)
+    q, k, v, do = (to_device(x, dtype, gpu) for x in (qb, kb, vb, dob))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=gpu)
+    runs = []
+    for _ in range(2):
+        dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, 1 / math.sqrt(d), True, ws)
+        torch.cuda.synchronize()
+        runs.append((dq, dk, dv))
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+    dq_h, dk_h, dv_h = (to_host_f64(x) for x in runs[0])
+    for x in (dq_h, dk_h, dv_h):
+        assert np.isfinite(x).all()
+    # every head: sum_j dV_j = sum_i dO_i (probability rows sum to 1) and sum_j dK_j = 0
+    dow = fa_inputs.widen(dob, dtype)
+    assert max_abs(dv_h.sum(axis=2), dow.sum(axis=2)) <= 0.5
+    assert np.abs(dk_h.sum(axis=2)).max() <= 0.5
+    scale = float(np.float32(1 / math.sqrt(d)))
+    for bh in (0, (B * H) // 2, B * H - 1):
+        b, h = divmod(bh, H)
+        sub = [fa_inputs.widen(x[b:b + 1, h:h + 1], dtype) for x in (qb, kb, vb, dob)]
+        rq, rk, rv = oracle.bwd_heads(*sub, scale, True, [0])
+        say(f"  head {bh}")
+        compare("dQ", dq_h[b, h], rq[0])
+        compare("dK", dk_h[b, h], rk[0])
+        compare("dV", dv_h[b, h], rv[0])
+
