@@ -330,6 +330,26 @@ def sweep(fa, device, steps, warmup, only=None):
                      "bwd_ms": bms, "bwd_tflops": f_bwd / (bms * 1e-3) / 1e12}
         log(f"[bench] sweep {name}: fwd {fms:.3f} ms ({res[name]['fwd_tflops']:.0f} TFLOP/s)  "
             f"bwd {bms:.3f} ms ({res[name]['bwd_tflops']:.0f} TFLOP/s nominal)")
+        if not padded and not causal:
+            # a grid of equal workgroups that fills the resident slots 1.33
+            # times (C2): the split-over-keys entry point, whose plan fills
+            # whole rounds, on the same inputs
+            wss = torch.empty(fa.fa_fwd_splitkv_workspace_size(B, H, N, N, d), dtype=torch.uint8, device=device)
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+            for i in range(warmup + steps):
+                e = evs[i - warmup] if i >= warmup else None
+                if e:
+                    e[0].record(stream)
+                fa.fa_fwd_splitkv(q, k, v, o, lse, None, None, scale, causal, wss, stream)
+                if e:
+                    e[1].record(stream)
+            torch.cuda.synchronize()
+            sms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+            res[name]["splitkv_fwd_ms"] = sms
+            res[name]["splitkv_fwd_tflops"] = f_fwd / (sms * 1e-3) / 1e12
+            log(f"[bench] sweep {name} through fa_fwd_splitkv: fwd {sms:.3f} ms "
+                f"({res[name]['splitkv_fwd_tflops']:.0f} TFLOP/s)")
+            del wss
         del q, k, v, do, o, lse, dq, dk, dv, ws
     return res
 
