@@ -197,11 +197,10 @@ void fwd_kernel(FwdParams p) {
   const uint32_t kv_bytes = (uint32_t)Lk * RB;
   auto issue_tile = [&](const char *head, int t, char *slot, const uint32_t (&offs)[BPW]) {
     const bool ok = t >= t_beg && t < t_end;
-    // wave-uniform values, computed with scalar instructions (no clamped
-    // vector subtract): the resource's size is the valid bytes left from the tile on
-    const uint32_t tb = ok ? (uint32_t)t * TB : 0u;
-    const int rem = (int)kv_bytes - (int)tb;
-    const uint32_t n = ok && rem > 0 ? (uint32_t)rem : 0u;
+    // the values are wave-uniform; readfirstlane keeps them (and the resource)
+    // in SGPRs.  Unsigned: a head's K or V may span up to 2^32 - 1 bytes.
+    const uint32_t tb = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)t * TB : 0u);
+    const uint32_t n = __builtin_amdgcn_readfirstlane(ok && tb < kv_bytes ? kv_bytes - tb : 0u);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(head + tb), n);
 #pragma unroll
     for (int j = 0; j < BPW; ++j) dma16(r, slot + (w * BPW + j) * 1024, offs[j]);

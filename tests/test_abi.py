@@ -151,3 +151,14 @@ def test_noalloc_limits_without_gpu():
         assert lib.fa_bwd_noalloc(*args(4, 32, rows // 128)) == 7
         assert lib.fa_bwd_noalloc(*args(1, 1, rows)) == 7
 
+
+def test_head_size_limit_without_gpu():
+    # one head is addressed through a 32-bit buffer resource: N * d * 2 < 2^32
+    for d, nmax in ((128, (1 << 32) // 256 - 1), (64, (1 << 32) // 128 - 1)):
+        assert fa.fa_fwd_plan(1, 1, nmax, d, 0, fa.FA_BF16).grid > 0
+        with pytest.raises(fa.FaError) as e:
+            fa.fa_fwd_plan(1, 1, nmax + 1, d, 0, fa.FA_BF16)
+        assert e.value.status == 2
+        assert fa.fa_bwd_workspace_size(1, 1, nmax, d) > 0
+        assert fa.fa_bwd_workspace_size(1, 1, nmax + 1, d) == 0
+
