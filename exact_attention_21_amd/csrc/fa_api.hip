@@ -1,7 +1,10 @@
 // C-ABI layer: argument validation, launch planning, device gating and kernel
 // launches for the fused attention library.  No allocation; global mutable
 // state is limited to per-device caches (the "is gfx950" check and the device
-// address of the no-allocation backward's static scratch array).
+// address of the no-allocation backward's static scratch array).  In debug
+// mode (FA_DEBUG) each computing entry point prints its plan once its
+// arguments have passed the host checks, before the device check, and after
+// its launches the counts of non-finite values in its inputs and outputs.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -112,6 +115,23 @@ int fwd_qb(int N, int d) { return d == 128 ? FWD_QB_D128 : (N > 128 ? FWD_QB_D64
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Debug mode, after the launches of one call: the launch error, or the
+// non-finite counts of the listed tensors (not while the stream is being
+// captured: the scan waits for the stream).
+void debug_after(const char *fn, hipError_t e, hipStream_t st,
+                 std::initializer_list<fa::DebugTensor> ts) {
+  if (e != hipSuccess) {
+    fa::debug_print("%s: launch failed: %s", fn, hipGetErrorString(e));
+    return;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone) {
+    fa::debug_print("%s: stream is being captured; no scan", fn);
+    return;
+  }
+  fa::debug_scan(fn, st, ts.begin(), (int)ts.size());
+}
+
 // Key chunks of the split forward.  Its workgroups all carry about the same
 // work, and the GPU holds 768 of them at once (256 CUs x 3), so the chunk count
 // is chosen by how well the grid fills whole rounds of 768: the smallest count
@@ -213,9 +233,9 @@ int fa_fwd_plan(int B, int H, int N, int d, int causal, int dtype, fa_plan_t *pl
 
 namespace {
 
-int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, const int *lq,
-             const int *lk, int B, int H, int Nq, int Nk, int d, float scale, int causal,
-             float dropout_p, uint64_t seed, uint32_t offset, int dtype, void *stream) {
+int fwd_impl(const char *fn, const void *q, const void *k, const void *v, void *o, float *lse,
+             const int *lq, const int *lk, int B, int H, int Nq, int Nk, int d, float scale,
+             int causal, float dropout_p, uint64_t seed, uint32_t offset, int dtype, void *stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   fa_plan_t plan;
   int rc = fa_fwd_plan(B, H, Nq, d, causal, dtype, &plan);
@@ -229,6 +249,14 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, c
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   if (!aligned4(lq) || !aligned4(lk)) return FA_ERR_ALIGN;
+  const bool dbg = fa::debug_enabled();
+  if (dbg)
+    fa::debug_print("%s: B=%d H=%d Nq=%d Nk=%d d=%d dtype=%s causal=%d scale=%g dropout_p=%g "
+                    "seqlens=%s; grid %d x %d threads, %d query rows and %d-key tiles per "
+                    "workgroup, %d bytes of LDS, xcd_grouped=%d",
+                    fn, B, H, Nq, Nk, d, dtype == FA_BF16 ? "bf16" : "f16", causal, scale,
+                    dropout_p, lq || lk ? "per sequence" : "full", plan.grid, plan.threads,
+                    plan.block_m, plan.block_n, plan.lds_bytes, plan.xcd_grouped);
   rc = check_device();
   if (rc) return rc;
   p.q = q;
@@ -240,8 +268,13 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, c
   p.n_qtiles = (Nq + plan.block_m - 1) / plan.block_m;
   p.xcd_grouped = plan.xcd_grouped;
   p.scale_log2 = scale * 1.4426950408889634f;
-  const hipError_t e = fa::launch_fwd(p, dtype, d, causal, plan.block_m / 128, plan.grid,
-                                      reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = fa::launch_fwd(p, dtype, d, causal, plan.block_m / 128, plan.grid, st);
+  if (dbg) {
+    const size_t nq = (size_t)B * H * Nq, nk = (size_t)B * H * Nk;
+    debug_after(fn, e, st, {{"q", q, nq * d, dtype}, {"k", k, nk * d, dtype}, {"v", v, nk * d, dtype},
+                            {"o", o, nq * d, dtype}, {"lse", lse, nq, 2}});
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -251,23 +284,23 @@ extern "C" {
 
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
            int N, int d, float scale, int causal, int dtype, void *stream) {
-  return fwd_impl(q, k, v, o, lse, nullptr, nullptr, B, H, N, N, d, scale, causal, 0.f, 0, 0, dtype,
-                  stream);
+  return fwd_impl("fa_fwd", q, k, v, o, lse, nullptr, nullptr, B, H, N, N, d, scale, causal, 0.f, 0,
+                  0, dtype, stream);
 }
 
 int fa_fwd_padded(const void *q, const void *k, const void *v, void *o, float *lse,
                   const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
                   int d, float scale, int causal, int dtype, void *stream) {
-  return fwd_impl(q, k, v, o, lse, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale, causal, 0.f, 0, 0,
-                  dtype, stream);
+  return fwd_impl("fa_fwd_padded", q, k, v, o, lse, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale,
+                  causal, 0.f, 0, 0, dtype, stream);
 }
 
 int fa_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *lse,
                    const int *seqlens_q, const int *seqlens_k, int B, int H, int Nq, int Nk,
                    int d, float scale, int causal, float dropout_p, uint64_t seed,
                    uint32_t offset, int dtype, void *stream) {
-  return fwd_impl(q, k, v, o, lse, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale, causal, dropout_p,
-                  seed, offset, dtype, stream);
+  return fwd_impl("fa_fwd_dropout", q, k, v, o, lse, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale,
+                  causal, dropout_p, seed, offset, dtype, stream);
 }
 
 size_t fa_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d) {
@@ -295,6 +328,15 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     return FA_ERR_ALIGN;
   if (!aligned4(seqlens_q) || !aligned4(seqlens_k)) return FA_ERR_ALIGN;
   if (workspace_bytes < split_workspace_bytes(B, H, Nq, d, sp)) return FA_ERR_WORKSPACE;
+  const bool dbg = fa::debug_enabled();
+  if (dbg)
+    fa::debug_print("fa_fwd_splitkv: B=%d H=%d Nq=%d Nk=%d d=%d dtype=%s causal=%d scale=%g "
+                    "seqlens=%s; %s: %d partials per query block of %d rows, %d keys each; "
+                    "grid %lld x 256 threads, then the merge (one wave per row)",
+                    B, H, Nq, Nk, d, dtype == FA_BF16 ? "bf16" : "f16", causal, scale,
+                    seqlens_q || seqlens_k ? "per sequence" : "full",
+                    decode ? "decode (one partial per wave)" : "split forward", sp.nsplit, sp.bm,
+                    sp.chunk, grid);
   rc = check_device();
   if (rc) return rc;
   fa::FwdParams p;
@@ -318,6 +360,12 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
   hipError_t e = decode ? fa::launch_fwd_decode(p, dtype, d, (int)grid, st)
                         : fa::launch_fwd_split(p, dtype, d, causal, (int)grid, st);
   if (e == hipSuccess) e = fa::launch_fwd_combine(p, dtype, d, (long)B * H * Nq, st);
+  if (dbg) {
+    const size_t nq = (size_t)B * H * Nq, nk = (size_t)B * H * Nk;
+    debug_after("fa_fwd_splitkv", e, st,
+                {{"q", q, nq * d, dtype}, {"k", k, nk * d, dtype}, {"v", v, nk * d, dtype},
+                 {"o", o, nq * d, dtype}, {"lse", lse, nq, 2}});
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -383,6 +431,25 @@ bool all_aligned(std::initializer_list<const void *> ptrs) {
   return true;
 }
 
+// Debug mode: the plan of a backward call (its passes and their grids).
+void debug_bwd_plan(const char *fn, const char *passes, int B, int H, int Nq, int Nk, int d,
+                    int dtype, int causal, float scale, float dropout_p, bool per_seq,
+                    const fa::BwdParams &p, const fa_plan_t &plan) {
+  fa::debug_print("%s: B=%d H=%d Nq=%d Nk=%d d=%d dtype=%s causal=%d scale=%g dropout_p=%g "
+                  "seqlens=%s; %s; dQ grid %lld (%d query rows per workgroup), dK/dV grid %lld "
+                  "(%d keys per workgroup, %d-row query blocks, %d bytes of LDS), xcd_grouped=%d",
+                  fn, B, H, Nq, Nk, d, dtype == FA_BF16 ? "bf16" : "f16", causal, scale, dropout_p,
+                  per_seq ? "per sequence" : "full", passes, (long long)p.n_qtiles * B * H,
+                  fa::BWD_DQ_BM, (long long)p.n_ktiles * B * H, plan.block_n, plan.block_m,
+                  plan.lds_bytes, plan.xcd_grouped);
+}
+
+// the two fp32 arrays of the backward workspace, for the debug scan
+fa::DebugTensor ws_neg_d(const fa::BwdParams &p, size_t rows) { return {"workspace -D", p.dws, rows, 2}; }
+fa::DebugTensor ws_lse2(const fa::BwdParams &p, size_t rows) {
+  return {"workspace LSE*log2(e)", p.lse2, rows, 2};
+}
+
 }  // namespace
 
 extern "C" {
@@ -396,13 +463,23 @@ int fa_bwd_preprocess(const void *o, const void *dout, const float *lse, int B, 
                      &p, &plan);
   if (rc) return rc;
   if (!all_aligned({o, dout, lse})) return FA_ERR_ALIGN;
+  const bool dbg = fa::debug_enabled();
+  if (dbg)
+    fa::debug_print("fa_bwd_preprocess: B=%d H=%d N=%d d=%d dtype=%s; one wave per row",
+                    B, H, N, d, dtype == FA_BF16 ? "bf16" : "f16");
   rc = check_device();
   if (rc) return rc;
   p.o = o;
   p.dout = dout;
   p.lse = lse;
-  const hipError_t e = fa::launch_bwd_pre(p, dtype, d, (long)B * H * N,
-                                          reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = fa::launch_bwd_pre(p, dtype, d, (long)B * H * N, st);
+  if (dbg) {
+    const size_t rows = (size_t)B * H * N;
+    debug_after("fa_bwd_preprocess", e, st,
+                {{"o", o, rows * d, dtype}, {"dout", dout, rows * d, dtype}, {"lse", lse, rows, 2},
+                 ws_neg_d(p, rows), ws_lse2(p, rows)});
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -416,6 +493,10 @@ int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, v
                      workspace_bytes, &p, &plan);
   if (rc) return rc;
   if (!all_aligned({q, k, v, dout, dk, dv})) return FA_ERR_ALIGN;
+  const bool dbg = fa::debug_enabled();
+  if (dbg)
+    debug_bwd_plan("fa_bwd_dkdv", "dK/dV pass only", B, H, N, N, d, dtype, causal, scale, 0.f, false,
+                   p, plan);
   rc = check_device();
   if (rc) return rc;
   p.q = q;
@@ -424,8 +505,14 @@ int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, v
   p.dout = dout;
   p.dk = dk;
   p.dv = dv;
-  const hipError_t e = fa::launch_bwd_dkdv(p, dtype, d, causal, p.n_ktiles * B * H,
-                                           reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = fa::launch_bwd_dkdv(p, dtype, d, causal, p.n_ktiles * B * H, st);
+  if (dbg) {
+    const size_t n = (size_t)B * H * N * d, rows = (size_t)B * H * N;
+    debug_after("fa_bwd_dkdv", e, st,
+                {{"q", q, n, dtype}, {"k", k, n, dtype}, {"v", v, n, dtype}, {"dout", dout, n, dtype},
+                 ws_neg_d(p, rows), ws_lse2(p, rows), {"dk", dk, n, dtype}, {"dv", dv, n, dtype}});
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -435,9 +522,9 @@ namespace {
 
 // dQ pass of the staged backward; with o and lse it also computes the row
 // statistics (the preprocessing step) instead of reading them
-int dq_stage(const void *q, const void *k, const void *v, const void *o, const void *dout,
-             const float *lse, void *dq, int B, int H, int N, int d, float scale, int causal,
-             int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+int dq_stage(const char *fn, const void *q, const void *k, const void *v, const void *o,
+             const void *dout, const float *lse, void *dq, int B, int H, int N, int d, float scale,
+             int causal, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
   fa::BwdParams p;
   fa_plan_t plan;
   int rc = bwd_setup(B, H, N, N, nullptr, nullptr, d, scale, causal, dtype, workspace,
@@ -445,6 +532,10 @@ int dq_stage(const void *q, const void *k, const void *v, const void *o, const v
   if (rc) return rc;
   const int pre = o != nullptr;
   if (!all_aligned({q, k, v, dout, dq}) || (pre && !all_aligned({o, lse}))) return FA_ERR_ALIGN;
+  const bool dbg = fa::debug_enabled();
+  if (dbg)
+    debug_bwd_plan(fn, pre ? "dQ pass with the row statistics" : "dQ pass only", B, H, N, N, d, dtype,
+                   causal, scale, 0.f, false, p, plan);
   rc = check_device();
   if (rc) return rc;
   p.q = q;
@@ -454,8 +545,20 @@ int dq_stage(const void *q, const void *k, const void *v, const void *o, const v
   p.dout = dout;
   p.lse = lse;
   p.dq = dq;
-  const hipError_t e = fa::launch_bwd_dq(p, dtype, d, causal, pre, p.n_qtiles * B * H,
-                                         reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = fa::launch_bwd_dq(p, dtype, d, causal, pre, p.n_qtiles * B * H, st);
+  if (dbg) {
+    const size_t n = (size_t)B * H * N * d, rows = (size_t)B * H * N;
+    if (pre)
+      debug_after(fn, e, st,
+                  {{"q", q, n, dtype}, {"k", k, n, dtype}, {"v", v, n, dtype}, {"o", o, n, dtype},
+                   {"dout", dout, n, dtype}, {"lse", lse, rows, 2}, ws_neg_d(p, rows),
+                   ws_lse2(p, rows), {"dq", dq, n, dtype}});
+    else
+      debug_after(fn, e, st,
+                  {{"q", q, n, dtype}, {"k", k, n, dtype}, {"v", v, n, dtype}, {"dout", dout, n, dtype},
+                   ws_neg_d(p, rows), ws_lse2(p, rows), {"dq", dq, n, dtype}});
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -467,8 +570,8 @@ int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, voi
               int H, int N, int d, float scale, int causal, int dtype, void *workspace,
               size_t workspace_bytes, void *stream) {
   if (!q || !k || !v || !dout || !dq || !workspace) return FA_ERR_NULL;
-  return dq_stage(q, k, v, nullptr, dout, nullptr, dq, B, H, N, d, scale, causal, dtype, workspace,
-                  workspace_bytes, stream);
+  return dq_stage("fa_bwd_dq", q, k, v, nullptr, dout, nullptr, dq, B, H, N, d, scale, causal, dtype,
+                  workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_dq_preprocess(const void *q, const void *k, const void *v, const void *o,
@@ -476,18 +579,19 @@ int fa_bwd_dq_preprocess(const void *q, const void *k, const void *v, const void
                          float scale, int causal, int dtype, void *workspace,
                          size_t workspace_bytes, void *stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !workspace) return FA_ERR_NULL;
-  return dq_stage(q, k, v, o, dout, lse, dq, B, H, N, d, scale, causal, dtype, workspace,
-                  workspace_bytes, stream);
+  return dq_stage("fa_bwd_dq_preprocess", q, k, v, o, dout, lse, dq, B, H, N, d, scale, causal, dtype,
+                  workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
 
 namespace {
 
-int bwd_impl(const void *q, const void *k, const void *v, const void *o, const void *dout,
-             const float *lse, void *dq, void *dk, void *dv, const int *lq, const int *lk, int B,
-             int H, int Nq, int Nk, int d, float scale, int causal, float dropout_p, uint64_t seed,
-             uint32_t offset, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+int bwd_impl(const char *fn, const void *q, const void *k, const void *v, const void *o,
+             const void *dout, const float *lse, void *dq, void *dk, void *dv, const int *lq,
+             const int *lk, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+             float dropout_p, uint64_t seed, uint32_t offset, int dtype, void *workspace,
+             size_t workspace_bytes, void *stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
   fa::BwdParams p;
   fa_plan_t plan;
@@ -496,6 +600,10 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const v
   if (rc) return rc;
   if (!dropout_spec(dropout_p, seed, offset, &p.drop)) return FA_ERR_ARG;
   if (!all_aligned({q, k, v, o, dout, lse, dq, dk, dv})) return FA_ERR_ALIGN;
+  const bool dbg = fa::debug_enabled();
+  if (dbg)
+    debug_bwd_plan(fn, "dQ pass with the row statistics, then the dK/dV pass", B, H, Nq, Nk, d, dtype,
+                   causal, scale, dropout_p, lq || lk, p, plan);
   rc = check_device();
   if (rc) return rc;
   p.q = q;
@@ -511,6 +619,13 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const v
   // the dQ pass computes the row statistics the dK/dV pass then reads
   hipError_t e = fa::launch_bwd_dq(p, dtype, d, causal, 1, p.n_qtiles * B * H, st);
   if (e == hipSuccess) e = fa::launch_bwd_dkdv(p, dtype, d, causal, p.n_ktiles * B * H, st);
+  if (dbg) {
+    const size_t nq = (size_t)B * H * Nq, nk = (size_t)B * H * Nk;
+    debug_after(fn, e, st,
+                {{"q", q, nq * d, dtype}, {"k", k, nk * d, dtype}, {"v", v, nk * d, dtype},
+                 {"o", o, nq * d, dtype}, {"dout", dout, nq * d, dtype}, {"lse", lse, nq, 2},
+                 {"dq", dq, nq * d, dtype}, {"dk", dk, nk * d, dtype}, {"dv", dv, nk * d, dtype}});
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -522,8 +637,8 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            const float *lse, void *dq, void *dk, void *dv, int B, int H, int N, int d,
            float scale, int causal, int dtype, void *workspace, size_t workspace_bytes,
            void *stream) {
-  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, H, N, N, d, scale, causal,
-                  0.f, 0, 0, dtype, workspace, workspace_bytes, stream);
+  return bwd_impl("fa_bwd", q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, H, N, N, d, scale,
+                  causal, 0.f, 0, 0, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, const void *dout,
@@ -541,16 +656,16 @@ int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, c
   if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_DEVICE;
   void *ws = scratch_ptr(dev);
   if (!ws) return FA_ERR_DEVICE;
-  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, H, N, N, d, scale, causal,
-                  0.f, 0, 0, dtype, ws, kScratchBytes, stream);
+  return bwd_impl("fa_bwd_noalloc", q, k, v, o, dout, lse, dq, dk, dv, nullptr, nullptr, B, H, N, N,
+                  d, scale, causal, 0.f, 0, 0, dtype, ws, kScratchBytes, stream);
 }
 
 int fa_bwd_padded(const void *q, const void *k, const void *v, const void *o, const void *dout,
                   const float *lse, void *dq, void *dk, void *dv, const int *seqlens_q,
                   const int *seqlens_k, int B, int H, int Nq, int Nk, int d, float scale,
                   int causal, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
-  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale,
-                  causal, 0.f, 0, 0, dtype, workspace, workspace_bytes, stream);
+  return bwd_impl("fa_bwd_padded", q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, B, H, Nq,
+                  Nk, d, scale, causal, 0.f, 0, 0, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o, const void *dout,
@@ -558,8 +673,9 @@ int fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o, c
                    const int *seqlens_k, int B, int H, int Nq, int Nk, int d, float scale,
                    int causal, float dropout_p, uint64_t seed, uint32_t offset, int dtype,
                    void *workspace, size_t workspace_bytes, void *stream) {
-  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, B, H, Nq, Nk, d, scale,
-                  causal, dropout_p, seed, offset, dtype, workspace, workspace_bytes, stream);
+  return bwd_impl("fa_bwd_dropout", q, k, v, o, dout, lse, dq, dk, dv, seqlens_q, seqlens_k, B, H, Nq,
+                  Nk, d, scale, causal, dropout_p, seed, offset, dtype, workspace, workspace_bytes,
+                  stream);
 }
 
 }  // extern "C"

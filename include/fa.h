@@ -35,10 +35,23 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL =
  *     the null stream).  The return value reports argument and launch errors
  *     only; execution errors surface at the caller's next synchronisation.  No
- *     exception or abort crosses the ABI.  There is no global mutable state, so
- *     concurrent calls on different streams are safe.
+ *     exception or abort crosses the ABI.  Global mutable state is limited to
+ *     per-device caches and the static device arrays of fa_bwd_noalloc and of
+ *     debug mode, so concurrent calls on different streams are safe (except
+ *     overlapping fa_bwd_noalloc calls on one GPU, and debug mode's scans).
  *   - The device current at the call must be a gfx950 GPU, else FA_ERR_DEVICE
  *     (there is no fallback path).
+ *   - Debug mode: with the environment variable FA_DEBUG (or
+ *     FLASH_ATTENTION_DEBUG, the name the FA1-vs-FA2 page uses) set to anything
+ *     but "0" (read at every call), each entry point that launches kernels prints
+ *     its launch plan to stderr once its arguments have passed the host
+ *     checks (before the device check), and after its launches waits for
+ *     `stream` and prints, for each input and output, how many of its values
+ *     are NaN, +inf and -inf (in an LSE, -inf marks a row that sees no key).
+ *     This follows the advice to run a debug mode that looks for NaN values
+ *     (FA1-vs-FA2 page, section 6.2, troubleshooting).  Results are
+ *     unchanged; the call becomes synchronous.  While `stream` is being
+ *     captured into a graph the scan is skipped.  Off by default.
  */
 #ifndef FA_H_
 #define FA_H_
