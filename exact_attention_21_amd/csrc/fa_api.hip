@@ -75,8 +75,10 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // kernels keep a pair iff its random byte is >= p8 and scale kept weights by
 // 256 / (256 - p8).  Returns false for p outside [0, 255.5/256).
 bool dropout_spec(float p, uint64_t seed, uint32_t offset, fa::DropoutSpec *d) {
-  if (!std::isfinite(p) || p < 0.f) return false;
-  const long p8 = std::lrint((double)p * 256.0);
+  // range first: lrint of a value past the range of long is unspecified
+  const double x = (double)p * 256.0;
+  if (!(x >= 0.0 && x < 255.5)) return false;  // NaN fails both
+  const long p8 = std::lrint(x);  // round half to even: 255.5 would give 256
   if (p8 > 255) return false;
   d->p8 = (uint32_t)p8;
   d->k0 = (uint32_t)seed;

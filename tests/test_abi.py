@@ -162,3 +162,21 @@ def test_head_size_limit_without_gpu():
         assert fa.fa_bwd_workspace_size(1, 1, nmax, d) > 0
         assert fa.fa_bwd_workspace_size(1, 1, nmax + 1, d) == 0
 
+
+
+def test_dropout_probability_range_without_gpu():
+    # p is checked before it is rounded to 8 bits: a value past the range of
+    # the rounding (1e30, inf) is rejected, not wrapped to a small threshold
+    lib = fa.lib()
+    p = ctypes.c_void_p(64)
+
+    def call(prob):
+        return lib.fa_fwd_dropout(p, p, p, p, p, None, None, 1, 1, 16, 16, 64, ctypes.c_float(0.125), 0,
+                                  ctypes.c_float(prob), ctypes.c_uint64(1), ctypes.c_uint32(0), 0, None)
+
+    for bad in (1e30, float("inf"), float("nan"), -1e-3, 1.0, 255.5 / 256, 3e38):
+        assert call(bad) == 9, bad
+    import torch
+    if not torch.cuda.is_available():
+        for ok in (0.0, -0.0, 0.1, 255.4 / 256):
+            assert call(ok) == 7, ok
