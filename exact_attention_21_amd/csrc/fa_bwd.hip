@@ -356,19 +356,42 @@ void bwd_dq_kernel(BwdParams p) {
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2 % NS>;
 
+  // a step on a key tile with no visible pair for this wave: only its share
+  // of the loads and the barrier, which keep the workgroup's ring going
+  auto idle_step = [&](int t, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    issue_step(t + NS - 1, std::integral_constant<int, (SL + NS - 1) % NS>{});
+    wait_vmcnt<(NS - 2) * DMA_PER_STEP>();
+    barrier_only();
+  };
+  // causal: the key tiles from t_live on start past the last key this wave's
+  // last row sees (they would add exact zeros to dQ); the lower waves of a
+  // workgroup have up to three of them at the end of its range
+  const int last_key = wr0 + 31 + shift;
+  const int t_live = !CAUSAL ? nt : last_key < 0 ? 0 : min(nt, last_key / BN + 1);
+
   issue_step(0, S0{});
   if constexpr (NS == 3) issue_step(1, S1{});
   wait_vmcnt<(NS - 2) * DMA_PER_STEP>();
   barrier_only();
   int t = 0;
-  for (; t + NS <= nt; t += NS) {  // key tile t lives in slot t % NS
+  for (; t + NS <= t_live; t += NS) {  // key tile t lives in slot t % NS
     step(t, S0{});
     step(t + 1, S1{});
     if constexpr (NS == 3) step(t + 2, S2{});
   }
-  if (t < nt) step(t, S0{});
+  if (t < t_live) step(t, S0{});
   if constexpr (NS == 3) {
-    if (t + 1 < nt) step(t + 1, S1{});
+    if (t + 1 < t_live) step(t + 1, S1{});
+  }
+  for (int u = t_live; u < nt; ++u) {
+    const int sl = u % NS;
+    if (sl == 0)
+      idle_step(u, S0{});
+    else if (sl == 1)
+      idle_step(u, S1{});
+    else
+      idle_step(u, S2{});
   }
   wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
@@ -630,12 +653,42 @@ void bwd_dkdv_kernel(BwdParams p) {
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2 % NS>;
 
+  // a step on a query tile with no visible pair for this wave: only its
+  // share of the loads and the barrier, which keep the workgroup's ring going
+  auto idle_step = [&](int i, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    issue_step(i + NS - 1, std::integral_constant<int, (SL + NS - 1) % NS>{});
+    wait_dma(std::integral_constant<int, NS - 2>{});
+    barrier_only();
+  };
   const int nsteps = max(0, nqt - qt0);
+  // causal: the first i_live query tiles end before the first query that sees
+  // this wave's first key (they would add exact zeros to dK and dV); wave w
+  // of a workgroup on the diagonal has w of them
+  int i_live = 0;
+  if constexpr (CAUSAL) {
+    const int need = kw0 - shift - (BM - 1);  // query tiles must reach this row
+    i_live = need <= 0 ? 0 : min(nsteps, max(0, (need + BM - 1) / BM - qt0));
+  }
   issue_step(0, S0{});
   if constexpr (NS == 3) issue_step(1, S1{});
   wait_dma(std::integral_constant<int, NS - 2>{});
   barrier_only();
   int i = 0;
+  for (; i < i_live; ++i) {
+    const int sl = i % NS;
+    if (sl == 0)
+      idle_step(i, S0{});
+    else if (sl == 1)
+      idle_step(i, S1{});
+    else
+      idle_step(i, S2{});
+  }
+  // live steps up to the next multiple of NS, where the unrolled loop's slots start
+  if (i % NS == 1 && i < nsteps) step(i++, S1{});
+  if constexpr (NS == 3) {
+    if (i % NS == 2 && i < nsteps) step(i++, S2{});
+  }
   for (; i + NS <= nsteps; i += NS) {  // query tile qt0 + i lives in slot i % NS
     step(i, S0{});
     step(i + 1, S1{});

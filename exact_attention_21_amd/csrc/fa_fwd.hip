@@ -410,24 +410,47 @@ void fwd_kernel(FwdParams p) {
     wait_vmcnt<(NS - 2) * DMA_PER_STEP>();  // tiles for step t + 1 have landed
     barrier_only();
   };
+  // a step on a tile with no visible pair for this wave: only its share of
+  // the loads and the barrier, which keep the workgroup's ring going
+  auto idle_step = [&](int t, auto slot) {
+    constexpr int SL = decltype(slot)::value;
+    issue_step(t + NS - 1, std::integral_constant<int, (SL + NS - 1) % NS>{});
+    wait_vmcnt<(NS - 2) * DMA_PER_STEP>();
+    barrier_only();
+  };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
   using S2 = std::integral_constant<int, 2 % NS>;
+
+  // causal: the tiles from t_live on start past the last key this wave's
+  // last row sees (their softmax would add exact zeros); the lower waves of
+  // a workgroup have up to three of them at the end of its range
+  const int last_key = wr0 + QB * 32 - 1 + shift;
+  const int t_live = !CAUSAL ? t_end : last_key < 0 ? t_beg : max(t_beg, min(t_end, last_key / BN + 1));
 
   issue_step(t_beg, S0{});
   if constexpr (NS == 3) issue_step(t_beg + 1, S1{});
   wait_vmcnt<(NS - 2) * DMA_PER_STEP>();
   barrier_only();
   int t = t_beg;
-  for (; t + NS <= t_end; t += NS) {  // tile t lives in slot (t - t_beg) % NS
+  for (; t + NS <= t_live; t += NS) {  // tile t lives in slot (t - t_beg) % NS
     step(t, S0{});
     step(t + 1, S1{});
     if constexpr (NS == 3) step(t + 2, S2{});
   }
-  if (t < t_end) step(t, S0{});
+  if (t < t_live) step(t, S0{});
   if constexpr (NS == 3) {
-    if (t + 1 < t_end) step(t + 1, S1{});
+    if (t + 1 < t_live) step(t + 1, S1{});
+  }
+  for (int u = t_live; u < t_end; ++u) {
+    const int sl = (u - t_beg) % NS;
+    if (sl == 0)
+      idle_step(u, S0{});
+    else if (sl == 1)
+      idle_step(u, S1{});
+    else
+      idle_step(u, S2{});
   }
   wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
