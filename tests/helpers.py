@@ -39,6 +39,27 @@ def max_abs(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
 
 
+def ulp16(x, dtype: str) -> np.ndarray:
+    """Unit in the last place of |x| in the 16-bit storage type (elementwise)."""
+    mant, emin = (7, -126) if dtype == "bf16" else (10, -14)
+    e = np.floor(np.log2(np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** emin)))
+    return 2.0 ** (e - mant)
+
+
+def grad_abs_excess(got, want, dtype: str) -> float:
+    """Largest |got - want| beyond max(TOL_GRAD_ABS, one 16-bit ulp of the
+    larger magnitude) over all elements (<= 0 passes).  The gradients are
+    stored in 16 bits, so an entry whose magnitude makes one unit in the last
+    place exceeds the absolute bar (|x| >= 8 in bf16, >= 64 in fp16) is held to that unit:
+    rounding the exact value alone can be that far off when the fp32 result
+    sits on the other side of a rounding midpoint."""
+    g, w = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    if g.size == 0:
+        return 0.0
+    bar = np.maximum(TOL_GRAD_ABS, ulp16(np.maximum(np.abs(g), np.abs(w)), dtype))
+    return float(np.max(np.abs(g - w) - bar))
+
+
 def rel_frob(a, b) -> float:
     ref = np.asarray(b, np.float64)
     den = float(np.linalg.norm(ref))

@@ -5,7 +5,10 @@ ones), dropout or not.  Each case runs the padded (or dropout) forward and
 backward and, without dropout, the split-over-keys forward too.  Bars as in
 the other parity tests: O max-abs <= 2e-2 (bf16) / 4e-3 (fp16), LSE <= 1e-3,
 gradients max-abs <= 5e-2 and rel-Frobenius <= 1e-2; rows that see no key are
-exactly O = 0, LSE = -inf.
+exactly O = 0, LSE = -inf.  A gradient entry large enough that one unit in the
+last place of its 16-bit storage exceeds 5e-2 (|x| >= 8 in bf16, as when
+one valid key collects the gradients of hundreds of rows) is held to that
+unit instead: the rounding of the stored value alone can reach it.
 
 The rel-Frobenius bar of dQ and dK is widened by a bound computed per case:
 the backward forms D = rowsum(dO * O) from the 16-bit O it is given, and with
@@ -20,9 +23,17 @@ where P K is the oracle's forward with V = K and P^T X the oracle's dV for the
 upstream gradient X.  dQ and dK must be within 1e-2 + 2 |delta| / |ref|
 (twice: the O the GPU hands its backward is within about one unit in the last
 place of the exact O, the rounding within half of one); dV does not involve D
-and always has the plain 1e-2 bar.  Max-abs is checked in every case.
+and always has the plain 1e-2 bar.  The bar is checked multiplied out,
+|err| <= 1e-2 |ref| + 2 |delta|, so that it also holds where the reference is
+exactly zero: over a single visible key P = 1 and D = dP, so dS = P (dP - D)
+vanishes identically and dQ = dK = 0, while the D formed from the rounded O
+leaves a gradient of the size of delta; where delta is zero too (O = V
+exactly), the fp32 difference dP - D leaves round-off, which an rms floor of
+1e-4 per element (500x below the max-abs bar) admits.  Max-abs is checked in
+every case.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -30,13 +41,16 @@ import pytest
 import exact_attention_21_amd as fa
 import fa_inputs
 import oracle
-from tests.helpers import (TOL_GRAD_ABS, TOL_GRAD_RELF, TOL_LSE, TOL_O, max_abs, rel_frob, say,
-                           to_device, to_host_f64)
+from tests.helpers import (TOL_GRAD_RELF, TOL_LSE, TOL_O, grad_abs_excess, max_abs, rel_frob, say, to_device,
+                           to_host_f64)
 from tests.test_padded_gpu import inputs, lens_tensor
 
 pytestmark = pytest.mark.gpu
 
-NCASES = 64
+# 64 cases by default; FA_RANDOM_SHAPE_CASES=n runs the first n of the same
+# seeded sequence (a longer sweep for kernel changes)
+NCASES = int(os.environ.get("FA_RANDOM_SHAPE_CASES", "64"))
+RMS_FLOOR = 1e-4  # 500x below the max-abs bar
 DROP_SEED = 0x5EEDFACE12345678
 
 
@@ -94,27 +108,29 @@ def test_random_shape(gpu, i):
         check_fwd(to_host_f64(split[0]), to_host_f64(split[1]), ro, rl, dtype, "split forward")
     ref = oracle.bwd_padded(*w, scale, causal, lq, lk, dropout=drop)
     live_rows = int(np.isfinite(rl).sum())
-    sens = d_rounding_sensitivity(w, ro, ref, scale, causal, lq, lk, dtype)
+    delta = d_rounding_delta(w, ro, scale, causal, lq, lk, dtype)
     for name, got, want in zip(("dQ", "dK", "dV"), grads, ref):
         g = to_host_f64(got)
         ea, er = max_abs(g, want), rel_frob(g, want)
-        bar = TOL_GRAD_RELF + 2.0 * sens.get(name, 0.0)
-        say(f"    {name}: max-abs {ea:.3e} rel-F {er:.3e} (bar {bar:.3e}; {live_rows} live rows)")
-        assert ea <= TOL_GRAD_ABS, (name, ea)
-        assert er <= bar, (name, er, bar)
+        # rel-F <= 1e-2 + 2 |delta| / |ref|, multiplied out so that it also
+        # holds where the reference is exactly zero, plus an rms floor of
+        # RMS_FLOOR per element for the fp32 round-off left where it is
+        err, den = float(np.linalg.norm(g - want)), float(np.linalg.norm(want))
+        allowed = TOL_GRAD_RELF * den + 2.0 * delta.get(name, 0.0) + RMS_FLOOR * math.sqrt(g.size)
+        say(f"    {name}: max-abs {ea:.3e} rel-F {er:.3e} (|err| {err:.3e}, allowed {allowed:.3e}; "
+            f"{live_rows} live rows)")
+        assert grad_abs_excess(g, want, dtype) <= 0.0, (name, ea)
+        assert err <= allowed, (name, err, allowed)
 
 
-def d_rounding_sensitivity(w, ro, ref, scale, causal, lq, lk, dtype):
-    """Relative change of the oracle's dQ and dK when D is formed from its own O
-    rounded to the storage dtype (exact: the gradients are affine in D)."""
+def d_rounding_delta(w, ro, scale, causal, lq, lk, dtype):
+    """Frobenius norm of the change of the oracle's dQ and dK when D is formed
+    from its own O rounded to the storage dtype (exact: the gradients are
+    affine in D)."""
     q, k, v, do = w
     o16 = fa_inputs.widen(fa_inputs.narrow(ro, dtype), dtype)
     dD = np.sum(do * (o16 - ro), axis=-1)                      # [B, H, Nq]
     pk, _ = oracle.fwd_padded(q, k, k, scale, causal, lq, lk)  # P K
     delta_dq = -scale * dD[..., None] * pk
     delta_dk = -scale * oracle.bwd_padded(q, k, v, dD[..., None] * q, scale, causal, lq, lk)[2]  # P^T (dD Q)
-    out = {}
-    for name, delta, want in (("dQ", delta_dq, ref[0]), ("dK", delta_dk, ref[1])):
-        den = float(np.linalg.norm(want))
-        out[name] = float(np.linalg.norm(delta)) / den if den > 0 else 0.0
-    return out
+    return {"dQ": float(np.linalg.norm(delta_dq)), "dK": float(np.linalg.norm(delta_dk))}
