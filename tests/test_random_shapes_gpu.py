@@ -70,6 +70,27 @@ def draw_case(i: int):
     return B, H, Nq, Nk, d, dtype, causal, lq, lk, p
 
 
+# Larger shapes: several tiles per head, up to 32 heads (B*H a multiple of 8
+# selects the XCD-grouped dispatch), Nq and Nk up to 1500
+NCASES_LARGE = int(os.environ.get("FA_RANDOM_LARGE_CASES", "12"))
+
+
+def draw_large_case(i: int):
+    rng = np.random.default_rng(0xB16C0000 + i)
+    B, H = int(rng.integers(1, 5)), int(rng.choice([1, 2, 4, 8]))
+    Nq = 1 if rng.random() < 0.1 else int(rng.integers(1, 1501))
+    Nk = Nq if rng.random() < 0.4 else int(rng.integers(1, 1501))
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f16"]))
+    causal = bool(rng.random() < 0.5)
+    lq = lk = None
+    if rng.random() < 0.5:
+        lq = [int(x) for x in rng.integers(0, Nq + 1, size=B)]
+        lk = [int(x) for x in rng.integers(0, Nk + 1, size=B)]
+    p = float(rng.choice([0.1, 0.3])) if rng.random() < 0.25 else 0.0
+    return B, H, Nq, Nk, d, dtype, causal, lq, lk, p
+
+
 def check_fwd(o, lse, ro, rl, dtype, what):
     dead = np.isneginf(rl)
     assert np.array_equal(np.isneginf(lse), dead), what
@@ -83,10 +104,23 @@ def check_fwd(o, lse, ro, rl, dtype, what):
 
 @pytest.mark.parametrize("i", range(NCASES))
 def test_random_shape(gpu, i):
+    say(f"[random {i}]")
+    run_case(gpu, draw_case(i), 7000 + i, i)
+
+
+@pytest.mark.parametrize("i", range(NCASES_LARGE))
+def test_random_large_shape(gpu, i):
+    say(f"[random large {i}]")
+    run_case(gpu, draw_large_case(i), 9000 + i, 1000 + i)
+
+
+def run_case(gpu, case, seed, i):
+    """One case through the padded (or dropout) forward and backward and the
+    split forward, against the oracle; i is the dropout offset."""
     import torch
-    B, H, Nq, Nk, d, dtype, causal, lq, lk, p = draw_case(i)
-    say(f"[random {i}] B={B} H={H} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal} lq={lq} lk={lk} p={p}")
-    q, k, v, do = inputs(Nq, Nk, d, dtype, 7000 + i, B=B, H=H)
+    B, H, Nq, Nk, d, dtype, causal, lq, lk, p = case
+    say(f"    B={B} H={H} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal} lq={lq} lk={lk} p={p}")
+    q, k, v, do = inputs(Nq, Nk, d, dtype, seed, B=B, H=H)
     tq, tk, tv, tdo = (to_device(x, dtype, gpu) for x in (q, k, v, do))
     Lq, Lk = lens_tensor(lq, gpu), lens_tensor(lk, gpu)
     if p > 0:
