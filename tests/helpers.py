@@ -46,17 +46,18 @@ def ulp16(x, dtype: str) -> np.ndarray:
     return 2.0 ** (e - mant)
 
 
-def grad_abs_excess(got, want, dtype: str) -> float:
+def grad_abs_excess(got, want, dtype: str, slack=0.0) -> float:
     """Largest |got - want| beyond max(TOL_GRAD_ABS, one 16-bit ulp of the
-    larger magnitude) over all elements (<= 0 passes).  The gradients are
-    stored in 16 bits, so an entry whose magnitude makes one unit in the last
-    place exceeds the absolute bar (|x| >= 8 in bf16, >= 64 in fp16) is held to that unit:
-    rounding the exact value alone can be that far off when the fp32 result
-    sits on the other side of a rounding midpoint."""
+    larger magnitude) + slack over all elements (<= 0 passes; slack may be an
+    array of the same shape).  The gradients are stored in 16 bits, so an
+    entry whose magnitude makes one unit in the last place exceed the absolute
+    bar (|x| >= 8 in bf16, >= 64 in fp16) is held to that unit: rounding the
+    exact value alone can be that far off when the fp32 result sits on the
+    other side of a rounding midpoint."""
     g, w = np.asarray(got, np.float64), np.asarray(want, np.float64)
     if g.size == 0:
         return 0.0
-    bar = np.maximum(TOL_GRAD_ABS, ulp16(np.maximum(np.abs(g), np.abs(w)), dtype))
+    bar = np.maximum(TOL_GRAD_ABS, ulp16(np.maximum(np.abs(g), np.abs(w)), dtype)) + slack
     return float(np.max(np.abs(g - w) - bar))
 
 

@@ -30,7 +30,9 @@ vanishes identically and dQ = dK = 0, while the D formed from the rounded O
 leaves a gradient of the size of delta; where delta is zero too (O = V
 exactly), the fp32 difference dP - D leaves round-off, which an rms floor of
 1e-4 per element (500x below the max-abs bar) admits.  Max-abs is checked in
-every case.
+every case, with the same change as slack element by element (2 |delta_ij|):
+where dS cancels for every row (one visible key), the rounded O's effect on D
+sums over all of the rows into that key's dK.
 """
 import math
 import os
@@ -149,22 +151,25 @@ def run_case(gpu, case, seed, i):
         # rel-F <= 1e-2 + 2 |delta| / |ref|, multiplied out so that it also
         # holds where the reference is exactly zero, plus an rms floor of
         # RMS_FLOOR per element for the fp32 round-off left where it is
+        dl = delta.get(name)
         err, den = float(np.linalg.norm(g - want)), float(np.linalg.norm(want))
-        allowed = TOL_GRAD_RELF * den + 2.0 * delta.get(name, 0.0) + RMS_FLOOR * math.sqrt(g.size)
+        allowed = TOL_GRAD_RELF * den + (2.0 * float(np.linalg.norm(dl)) if dl is not None else 0.0) \
+            + RMS_FLOOR * math.sqrt(g.size)
         say(f"    {name}: max-abs {ea:.3e} rel-F {er:.3e} (|err| {err:.3e}, allowed {allowed:.3e}; "
             f"{live_rows} live rows)")
-        assert grad_abs_excess(g, want, dtype) <= 0.0, (name, ea)
+        # max-abs: the same exact change, element by element
+        slack = 2.0 * np.abs(dl) if dl is not None else 0.0
+        assert grad_abs_excess(g, want, dtype, slack) <= 0.0, (name, ea)
         assert err <= allowed, (name, err, allowed)
 
 
 def d_rounding_delta(w, ro, scale, causal, lq, lk, dtype):
-    """Frobenius norm of the change of the oracle's dQ and dK when D is formed
-    from its own O rounded to the storage dtype (exact: the gradients are
-    affine in D)."""
+    """Change of the oracle's dQ and dK when D is formed from its own O rounded
+    to the storage dtype (exact: the gradients are affine in D)."""
     q, k, v, do = w
     o16 = fa_inputs.widen(fa_inputs.narrow(ro, dtype), dtype)
     dD = np.sum(do * (o16 - ro), axis=-1)                      # [B, H, Nq]
     pk, _ = oracle.fwd_padded(q, k, k, scale, causal, lq, lk)  # P K
     delta_dq = -scale * dD[..., None] * pk
     delta_dk = -scale * oracle.bwd_padded(q, k, v, dD[..., None] * q, scale, causal, lq, lk)[2]  # P^T (dD Q)
-    return {"dQ": float(np.linalg.norm(delta_dq)), "dK": float(np.linalg.norm(delta_dk))}
+    return {"dQ": delta_dq, "dK": delta_dk}
