@@ -330,10 +330,28 @@ def sweep(fa, device, steps, warmup, only=None):
                      "bwd_ms": bms, "bwd_tflops": f_bwd / (bms * 1e-3) / 1e12}
         log(f"[bench] sweep {name}: fwd {fms:.3f} ms ({res[name]['fwd_tflops']:.0f} TFLOP/s)  "
             f"bwd {bms:.3f} ms ({res[name]['bwd_tflops']:.0f} TFLOP/s nominal)")
+        if not padded:
+            # the forward alone, back to back: in the loop above each forward
+            # follows a backward, which leaves other data in the caches
+            evr = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+            for i in range(warmup + steps):
+                e = evr[i - warmup] if i >= warmup else None
+                if e:
+                    e[0].record(stream)
+                fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
+                if e:
+                    e[1].record(stream)
+            torch.cuda.synchronize()
+            rms = sum(e[0].elapsed_time(e[1]) for e in evr) / steps
+            res[name]["fwd_repeat_ms"] = rms
+            res[name]["fwd_repeat_tflops"] = f_fwd / (rms * 1e-3) / 1e12
+            log(f"[bench] sweep {name}: forward back to back {rms:.3f} ms "
+                f"({res[name]['fwd_repeat_tflops']:.0f} TFLOP/s)")
         if not padded and not causal:
             # a grid of equal workgroups that fills the resident slots 1.33
             # times (C2): the split-over-keys entry point, whose plan fills
-            # whole rounds, on the same inputs
+            # whole rounds, on the same inputs (back to back, like the
+            # fwd_repeat figure it compares with)
             wss = torch.empty(fa.fa_fwd_splitkv_workspace_size(B, H, N, N, d), dtype=torch.uint8, device=device)
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
             for i in range(warmup + steps):
