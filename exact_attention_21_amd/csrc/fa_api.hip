@@ -270,6 +270,7 @@ int fwd_impl(const char *fn, const void *q, const void *k, const void *v, void *
   p.n_qtiles = (Nq + plan.block_m - 1) / plan.block_m;
   p.xcd_grouped = plan.xcd_grouped;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal_group = lq || lk ? fa::CAUSAL_GROUP_LENGTHS : fa::CAUSAL_GROUP_EQUAL;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = fa::launch_fwd(p, dtype, d, causal, plan.block_m / 128, plan.grid, st);
   if (dbg) {
@@ -352,6 +353,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
   p.n_qtiles = sp.n_qtiles;
   p.xcd_grouped = 0;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal_group = seqlens_q || seqlens_k ? fa::CAUSAL_GROUP_LENGTHS : fa::CAUSAL_GROUP_EQUAL;
   p.nsplit = sp.nsplit;
   p.chunk = sp.chunk;
   char *ws = static_cast<char *>(workspace);
@@ -424,6 +426,7 @@ int bwd_setup(int B, int H, int Nq, int Nk, const int *lq, const int *lk, int d,
   p->xcd_grouped = plan->xcd_grouped;
   p->scale = scale;
   p->scale_log2 = scale * 1.4426950408889634f;
+  p->causal_group = lq || lk ? fa::CAUSAL_GROUP_LENGTHS : fa::CAUSAL_GROUP_EQUAL;
   return FA_OK;
 }
 

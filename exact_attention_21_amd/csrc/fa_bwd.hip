@@ -150,7 +150,7 @@ void bwd_dq_kernel(BwdParams p) {
   {
     const int nq = p.n_qtiles;
     int r;
-    grid_tile((int)blockIdx.x, (int)gridDim.x / nq, nq, p.xcd_grouped, CAUSAL ? FA_CAUSAL_GROUP : 1, 0, bh, r);
+    grid_tile((int)blockIdx.x, (int)gridDim.x / nq, nq, p.xcd_grouped, CAUSAL ? p.causal_group : 1, 0, bh, r);
     qt = CAUSAL ? nq - 1 - r : r;  // causal: longest rows first
   }
   const int i0 = qt * BM;
@@ -458,7 +458,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   {
     const int nk = p.n_ktiles;
     // causal: key tile 0 sees every query tile, so ascending order is heavy-first
-    grid_tile((int)blockIdx.x, (int)gridDim.x / nk, nk, p.xcd_grouped, CAUSAL ? FA_CAUSAL_GROUP : 1, 0, bh, kt);
+    grid_tile((int)blockIdx.x, (int)gridDim.x / nk, nk, p.xcd_grouped, CAUSAL ? p.causal_group : 1, 0, bh, kt);
   }
   const int j0 = kt * BN;
   const int kw0 = j0 + 32 * w;

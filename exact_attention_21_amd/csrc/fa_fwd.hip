@@ -153,10 +153,10 @@ void fwd_kernel(FwdParams p) {
     const int bid = SPLIT ? (int)(blockIdx.x / (unsigned)p.nsplit) : (int)blockIdx.x;
     const int heads = (int)(gridDim.x / (SPLIT ? (unsigned)p.nsplit : 1u)) / nq;
     int r;
-    // causal: heads in pairs, and the last heads (two rounds of the FWD_OCC
+    // causal: heads in groups of p.causal_group, and the last heads (two rounds of the FWD_OCC
     // workgroups per CU of an XCD's 32 CUs, or of all 256 when the heads are
     // not grouped per XCD) in one group, so that the grid ends on short tiles
-    grid_tile(bid, heads, nq, p.xcd_grouped, CAUSAL ? FA_CAUSAL_GROUP : 1,
+    grid_tile(bid, heads, nq, p.xcd_grouped, CAUSAL ? p.causal_group : 1,
               CAUSAL ? causal_tail_heads(nq, (p.xcd_grouped ? 32 : 256) * FWD_OCC(D, QB, DROP)) : 0, bh, r);
     qt = CAUSAL ? nq - 1 - r : r;  // causal: longest rows first
   }

@@ -64,12 +64,14 @@ struct DropoutSpec {
   float scale;
 };
 
-// Causal grids: heads per dispatch group (see grid_tile).  Pairs: the grid
-// ends on shorter tiles than with one head at a time, while only two heads'
-// K/V per XCD are in use at once.
-#ifndef FA_CAUSAL_GROUP
-#define FA_CAUSAL_GROUP 2
-#endif
+// Causal grids: heads per dispatch group (see grid_tile), chosen by the host.
+// Four heads when every head has the same length: the grid ends on shorter
+// tiles than with fewer heads per group, while only a few heads' K/V per XCD
+// are in use at once.  Pairs when per-batch lengths are given: the rank order
+// inside a group is by tile index, which is by length only within one batch
+// entry, and a group of four spans two entries.
+constexpr int CAUSAL_GROUP_EQUAL = 4;
+constexpr int CAUSAL_GROUP_LENGTHS = 2;
 // Heads of the final dispatch group of an XCD that holds `slots` workgroups
 // at once: enough tiles for two rounds of its slots.
 __host__ __device__ constexpr int causal_tail_heads(int ntiles, int slots) {
@@ -90,6 +92,7 @@ struct FwdParams {
   int n_qtiles;     // ceil(Nq / BM)
   int xcd_grouped;  // 1: B*H is a multiple of 8 and heads are grouped per XCD
   float scale_log2; // scale * log2(e)
+  int causal_group; // causal: heads per dispatch group
 };
 
 // Backward tiling.  dQ pass: 128 query rows per workgroup, 32 keys per step.
@@ -129,7 +132,7 @@ struct BwdParams {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
-  float *dws;       // fp32 [B][H][Nq] workspace: D = rowsum(dO * O)
+  float *dws;       // fp32 [B][H][Nq] workspace: -D = -rowsum(dO * O)
   float *lse2;      // fp32 [B][H][Nq] workspace: LSE * log2(e) (+inf for rows with LSE = -inf)
   SeqShape seq;
   DropoutSpec drop;
@@ -138,9 +141,10 @@ struct BwdParams {
   int xcd_grouped;
   float scale;
   float scale_log2;
+  int causal_group;  // causal: heads per dispatch group
 };
 
-// D = rowsum(dO * O) and LSE * log2(e) (reads p.o, p.dout, p.lse; writes p.dws, p.lse2)
+// -D = -rowsum(dO * O) and LSE * log2(e) (reads p.o, p.dout, p.lse; writes p.dws, p.lse2)
 hipError_t launch_bwd_pre(const BwdParams &p, int dtype, int d, long rows, hipStream_t st);
 // dQ pass (reads q, k, v, dout, dws, lse2; writes dq); grid = n_qtiles * B * H.
 // pre != 0: it computes dws and lse2 itself (reads o and lse, writes dws, lse2)
