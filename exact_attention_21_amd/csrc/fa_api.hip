@@ -117,6 +117,12 @@ int fwd_qb(int N, int d) { return d == 128 ? FWD_QB_D128 : (N > 128 ? FWD_QB_D64
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// heads per dispatch group of a causal grid (see fa_kernels.h)
+int causal_group(const int *lq, const int *lk, int Nk, int d) {
+  const bool small = (long)Nk * d <= fa::CAUSAL_GROUP_SMALL_MAX_ND;
+  return !lq && !lk && small ? fa::CAUSAL_GROUP_SMALL : fa::CAUSAL_GROUP_PAIR;
+}
+
 // Debug mode, after the launches of one call: the launch error, or the
 // non-finite counts of the listed tensors (not while the stream is being
 // captured: the scan waits for the stream).
@@ -270,7 +276,7 @@ int fwd_impl(const char *fn, const void *q, const void *k, const void *v, void *
   p.n_qtiles = (Nq + plan.block_m - 1) / plan.block_m;
   p.xcd_grouped = plan.xcd_grouped;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.causal_group = lq || lk ? fa::CAUSAL_GROUP_LENGTHS : fa::CAUSAL_GROUP_EQUAL;
+  p.causal_group = causal_group(lq, lk, Nk, d);
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = fa::launch_fwd(p, dtype, d, causal, plan.block_m / 128, plan.grid, st);
   if (dbg) {
@@ -353,7 +359,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
   p.n_qtiles = sp.n_qtiles;
   p.xcd_grouped = 0;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.causal_group = seqlens_q || seqlens_k ? fa::CAUSAL_GROUP_LENGTHS : fa::CAUSAL_GROUP_EQUAL;
+  p.causal_group = causal_group(seqlens_q, seqlens_k, Nk, d);
   p.nsplit = sp.nsplit;
   p.chunk = sp.chunk;
   char *ws = static_cast<char *>(workspace);
@@ -426,7 +432,7 @@ int bwd_setup(int B, int H, int Nq, int Nk, const int *lq, const int *lk, int d,
   p->xcd_grouped = plan->xcd_grouped;
   p->scale = scale;
   p->scale_log2 = scale * 1.4426950408889634f;
-  p->causal_group = lq || lk ? fa::CAUSAL_GROUP_LENGTHS : fa::CAUSAL_GROUP_EQUAL;
+  p->causal_group = causal_group(lq, lk, Nk, d);
   return FA_OK;
 }
 

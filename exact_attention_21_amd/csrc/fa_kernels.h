@@ -65,13 +65,16 @@ struct DropoutSpec {
 };
 
 // Causal grids: heads per dispatch group (see grid_tile), chosen by the host.
-// Four heads when every head has the same length: the grid ends on shorter
-// tiles than with fewer heads per group, while only a few heads' K/V per XCD
-// are in use at once.  Pairs when per-batch lengths are given: the rank order
-// inside a group is by tile index, which is by length only within one batch
-// entry, and a group of four spans two entries.
-constexpr int CAUSAL_GROUP_EQUAL = 4;
-constexpr int CAUSAL_GROUP_LENGTHS = 2;
+// More heads per group end the grid on shorter tiles but keep more heads' K/V
+// in use on an XCD at once (more L2 misses).  Four heads when every head has
+// the same length and one head's K and V take at most 2 MiB (N d <= 2^19);
+// pairs otherwise: with larger heads four of them raised the L2 misses by a
+// third to a half for no measurable time, and with per-batch lengths the rank
+// order inside a group is by tile index, which is by length only within one
+// batch entry (a group of four spans two entries).
+constexpr int CAUSAL_GROUP_SMALL = 4;
+constexpr int CAUSAL_GROUP_PAIR = 2;
+constexpr long CAUSAL_GROUP_SMALL_MAX_ND = 1L << 19;
 // Heads of the final dispatch group of an XCD that holds `slots` workgroups
 // at once: enough tiles for two rounds of its slots.
 __host__ __device__ constexpr int causal_tail_heads(int ntiles, int slots) {
