@@ -121,8 +121,8 @@ __device__ __forceinline__ float group_sum(float x) {
 // run together and share its K/V in L2; larger groups interleave more heads
 // (more L2 traffic) but, with rank 0 the longest tile of a causal mask, end
 // the grid on shorter tiles; the tail group evens out the end of the grid.
-__device__ __forceinline__ void grid_tile(int bid, int heads, int ntiles, bool xcd_grouped, int group,
-                                          int tail, int &bh, int &rank) {
+__host__ __device__ __forceinline__ void grid_tile(int bid, int heads, int ntiles, bool xcd_grouped,
+                                                   int group, int tail, int &bh, int &rank) {
   const int lanes = xcd_grouped ? 8 : 1;                 // heads interleaved across XCDs
   const int x = xcd_grouped ? (bid & 7) : 0, kk = xcd_grouped ? (bid >> 3) : bid;
   const int hpx = heads / lanes;                         // heads of this XCD (or of the grid)
