@@ -126,8 +126,10 @@ int causal_group(const int *lq, const int *lk, int Nk, int d) {
 // Debug mode, after the launches of one call: the launch error, or the
 // non-finite counts of the listed tensors (not while the stream is being
 // captured: the scan waits for the stream).
+// With per-batch lengths (lq, lk) it prints those first.
 void debug_after(const char *fn, hipError_t e, hipStream_t st,
-                 std::initializer_list<fa::DebugTensor> ts) {
+                 std::initializer_list<fa::DebugTensor> ts, const int *lq = nullptr,
+                 const int *lk = nullptr, int B = 0, int Nq = 0, int Nk = 0) {
   if (e != hipSuccess) {
     fa::debug_print("%s: launch failed: %s", fn, hipGetErrorString(e));
     return;
@@ -137,6 +139,7 @@ void debug_after(const char *fn, hipError_t e, hipStream_t st,
     fa::debug_print("%s: stream is being captured; no scan", fn);
     return;
   }
+  if (lq || lk) fa::debug_lengths(fn, st, lq, lk, B, Nq, Nk);
   fa::debug_scan(fn, st, ts.begin(), (int)ts.size());
 }
 
@@ -282,7 +285,7 @@ int fwd_impl(const char *fn, const void *q, const void *k, const void *v, void *
   if (dbg) {
     const size_t nq = (size_t)B * H * Nq, nk = (size_t)B * H * Nk;
     debug_after(fn, e, st, {{"q", q, nq * d, dtype}, {"k", k, nk * d, dtype}, {"v", v, nk * d, dtype},
-                            {"o", o, nq * d, dtype}, {"lse", lse, nq, 2}});
+                            {"o", o, nq * d, dtype}, {"lse", lse, nq, 2}}, lq, lk, B, Nq, Nk);
   }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -374,7 +377,8 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     const size_t nq = (size_t)B * H * Nq, nk = (size_t)B * H * Nk;
     debug_after("fa_fwd_splitkv", e, st,
                 {{"q", q, nq * d, dtype}, {"k", k, nk * d, dtype}, {"v", v, nk * d, dtype},
-                 {"o", o, nq * d, dtype}, {"lse", lse, nq, 2}});
+                 {"o", o, nq * d, dtype}, {"lse", lse, nq, 2}},
+                seqlens_q, seqlens_k, B, Nq, Nk);
   }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -635,7 +639,8 @@ int bwd_impl(const char *fn, const void *q, const void *k, const void *v, const 
     debug_after(fn, e, st,
                 {{"q", q, nq * d, dtype}, {"k", k, nk * d, dtype}, {"v", v, nk * d, dtype},
                  {"o", o, nq * d, dtype}, {"dout", dout, nq * d, dtype}, {"lse", lse, nq, 2},
-                 {"dq", dq, nq * d, dtype}, {"dk", dk, nk * d, dtype}, {"dv", dv, nk * d, dtype}});
+                 {"dq", dq, nq * d, dtype}, {"dk", dk, nk * d, dtype}, {"dv", dv, nk * d, dtype}},
+                lq, lk, B, Nq, Nk);
   }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

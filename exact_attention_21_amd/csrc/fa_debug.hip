@@ -17,6 +17,8 @@
 #include <cstring>
 #include <initializer_list>
 #include <mutex>
+#include <string>
+#include <vector>
 
 #include "fa_kernels.h"
 
@@ -133,6 +135,29 @@ void debug_scan(const char *fn, hipStream_t st, const DebugTensor *tensors, int 
     }
     debug_print("%s: %s: %llu NaN, %llu +inf, %llu -inf of %zu values%s", fn, t.name, h[0], h[1], h[2], t.n,
                 t.kind == 2 ? " (an LSE of -inf marks a row that sees no key)" : "");
+  }
+}
+
+void debug_lengths(const char *fn, hipStream_t st, const int *lq, const int *lk, int B, int Nq, int Nk) {
+  for (int side = 0; side < 2; ++side) {
+    const int *dev = side ? lk : lq;
+    if (!dev || B < 1) continue;
+    const int N = side ? Nk : Nq;
+    std::vector<int> h((size_t)B);
+    if (hipMemcpyAsync(h.data(), dev, sizeof(int) * (size_t)B, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess) {
+      debug_print("%s: seqlens_%c: copy failed: %s", fn, side ? 'k' : 'q', hipGetErrorString(hipGetLastError()));
+      continue;
+    }
+    std::string list;
+    int bad = 0;
+    for (int b = 0; b < B; ++b) {
+      if (h[(size_t)b] < 0 || h[(size_t)b] > N) ++bad;
+      if (b < 16) list += (b ? ", " : "") + std::to_string(h[(size_t)b]);
+    }
+    if (B > 16) list += ", ...";
+    debug_print("%s: seqlens_%c (B=%d, N=%d): [%s]%s", fn, side ? 'k' : 'q', B, N, list.c_str(),
+                bad ? "; outside [0, N], clamped on the device" : "");
   }
 }
 

@@ -181,5 +181,8 @@ bool debug_enabled();
 void debug_print(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
 // Waits for the stream, then prints the NaN / +inf / -inf counts of each tensor.
 void debug_scan(const char *fn, hipStream_t st, const DebugTensor *t, int count);
+// Waits for the stream, then prints the per-batch valid lengths (device
+// arrays, either may be null) and whether any lies outside [0, N].
+void debug_lengths(const char *fn, hipStream_t st, const int *lq, const int *lk, int B, int Nq, int Nk);
 
 }  // namespace fa

@@ -47,7 +47,9 @@
  *     its launch plan to stderr once its arguments have passed the host
  *     checks (before the device check), and after its launches waits for
  *     `stream` and prints, for each input and output, how many of its values
- *     are NaN, +inf and -inf (in an LSE, -inf marks a row that sees no key).
+ *     are NaN, +inf and -inf (in an LSE, -inf marks a row that sees no key),
+ *     after the per-batch lengths if the call takes them (values outside
+ *     [0, N] are flagged: the kernels clamp them).
  *     This follows the advice to run a debug mode that looks for NaN values
  *     (FA1-vs-FA2 page, section 6.2, troubleshooting).  Results are
  *     unchanged; the call becomes synchronous.  While `stream` is being

@@ -4,7 +4,8 @@ its inputs and outputs; results are bit-identical to those without it.  The
 counts are checked against what the inputs fix: none on clean inputs; a NaN
 planted in one element of query row i shows as one NaN in q, a NaN in every
 element of O row i and in LSE row i; rows that see no key show as -inf in the
-LSE (one per such row), never as NaN."""
+LSE (one per such row), never as NaN.  Calls with per-batch lengths print
+them, flagging values outside [0, N] (the kernels clamp them)."""
 import re
 
 import numpy as np
@@ -90,7 +91,10 @@ def test_dead_rows_are_reported_as_minus_inf(gpu, monkeypatch, capfd):
         so, sl = fa.fwd_splitkv(q, k, v, lq, lk, causal=False)
         return (o, lse, so, sl, *fa.bwd_padded(q, k, v, o, do, lse, lq, lk, causal=False))
 
-    scan, _ = _run_twice(monkeypatch, capfd, run)
+    scan, err = _run_twice(monkeypatch, capfd, run)
+    for fn in ("fa_fwd_padded", "fa_fwd_splitkv", "fa_bwd_padded"):
+        assert f"[FA_DEBUG] {fn}: seqlens_q (B=3, N=130): [130, 77, 0]\n" in err, fn
+        assert f"[FA_DEBUG] {fn}: seqlens_k (B=3, N=300): [300, 33, 160]\n" in err, fn
     H = 2
     dead = H * sum(130 - x for x in Lq)
     assert dead == 366
@@ -139,3 +143,17 @@ def torch_empty_ws(q):
     import torch
     B, H, N, d = q.shape
     return torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=q.device)
+
+
+def test_out_of_range_lengths_are_flagged(gpu, monkeypatch, capfd):
+    # lengths past N are clamped on the device; debug mode says so
+    dtype, d = "f16", 64
+    qb, kb, vb, _ = inputs(40, 50, d, dtype, 4703, B=2, H=1)
+    q, k, v = (to_device(x, dtype, gpu) for x in (qb, kb, vb))
+    lq, lk = lens_tensor([40, 99], gpu), lens_tensor([-3, 50], gpu)
+    scan, err = _run_twice(monkeypatch, capfd, lambda: fa.fwd_padded(q, k, v, lq, lk, causal=True))
+    assert "seqlens_q (B=2, N=40): [40, 99]; outside [0, N], clamped on the device" in err
+    assert "seqlens_k (B=2, N=50): [-3, 50]; outside [0, N], clamped on the device" in err
+    # batch entry 0 sees no key (Lk clamped to 0): its 40 rows are dead
+    assert scan[("fa_fwd_padded", "lse")] == (0, 0, 40, 80)
+
