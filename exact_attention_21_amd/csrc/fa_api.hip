@@ -16,6 +16,7 @@
 #include <initializer_list>
 
 #include "fa.h"
+#include "fa_debug.h"
 #include "fa_kernels.h"
 
 // Scratch of fa_bwd_noalloc: the backward workspace (-D and LSE * log2(e), fp32,

@@ -20,7 +20,7 @@
 #include <string>
 #include <vector>
 
-#include "fa_kernels.h"
+#include "fa_debug.h"
 
 namespace {
 

@@ -170,19 +170,4 @@ hipError_t launch_fwd_combine(const FwdParams &p, int dtype, int d, long rows, h
 constexpr int fwd_decode_tile(int d) { return d == 128 ? 32 : 64; }
 hipError_t launch_fwd_decode(const FwdParams &p, int dtype, int d, int grid, hipStream_t st);
 
-// Debug mode (environment variable FA_DEBUG set to anything but "0").
-struct DebugTensor {
-  const char *name;
-  const void *ptr;
-  size_t n;   // elements
-  int kind;   // 0 fp16, 1 bf16 (the dtype codes of the C ABI), 2 fp32
-};
-bool debug_enabled();
-void debug_print(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
-// Waits for the stream, then prints the NaN / +inf / -inf counts of each tensor.
-void debug_scan(const char *fn, hipStream_t st, const DebugTensor *t, int count);
-// Waits for the stream, then prints the per-batch valid lengths (device
-// arrays, either may be null) and whether any lies outside [0, N].
-void debug_lengths(const char *fn, hipStream_t st, const int *lq, const int *lk, int B, int Nq, int Nk);
-
 }  // namespace fa
