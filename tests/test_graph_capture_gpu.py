@@ -3,7 +3,9 @@
 memset, so the captured launches replay on whatever the static buffers hold:
 each replay runs on new inputs copied in eagerly, with eager work and
 synchronisations between the replays, and is compared bitwise with eager
-calls (fa_fwd, fa_bwd with a workspace) on the same inputs."""
+calls (fa_fwd, fa_bwd with a workspace) on the same inputs.  Debug mode
+under capture prints its plan but skips its scan (which would wait for the
+stream)."""
 import math
 
 import pytest
@@ -61,3 +63,33 @@ def test_forward_and_noalloc_backward_replay(gpu, monkeypatch):
         assert torch.equal(o, eo) and torch.equal(lse, el)
         for name, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), eg):
             assert torch.equal(a, b), name
+
+
+def test_debug_mode_skips_its_scan_under_capture(gpu, monkeypatch, capfd):
+    # the scan waits for the stream, which a capture forbids: it is skipped,
+    # the plan is still printed, and the captured forward replays correctly
+    import torch
+    monkeypatch.setenv("FA_DEBUG", "1")
+    B, H, N, d, dtype = 1, 2, 300, 64, "f16"
+    q, k, v = (to_device(x, dtype, gpu) for x in fa_inputs.qkv_bits(B, H, N, d, dtype, seed=5400))
+    o, lse = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device=gpu)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.fa_fwd(q, k, v, o, lse, 0.125, True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    capfd.readouterr()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.fa_fwd(q, k, v, o, lse, 0.125, True)
+    err = capfd.readouterr().err
+    assert "[FA_DEBUG] fa_fwd: B=1 H=2 Nq=300" in err
+    assert "[FA_DEBUG] fa_fwd: stream is being captured; no scan" in err
+    monkeypatch.delenv("FA_DEBUG")
+    o.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    eo, el = fa.fwd(q, k, v, causal=True, scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o, eo) and torch.equal(lse, el)
