@@ -56,7 +56,9 @@ MEASURED_TRAFFIC = {
     "bytes": {"fwd_kernel": 3.634e9, "bwd_dq_kernel": 2.362e9,
               "bwd_dkdv_kernel": 1.935e9},
 }
-KERNEL_SOURCES = ["exact_attention_21_amd/csrc/fa_bwd.hip", "exact_attention_21_amd/csrc/fa_fwd.hip",
+KERNEL_SOURCES = ["exact_attention_21_amd/csrc/fa_bwd.hip", "exact_attention_21_amd/csrc/fa_bwd_common.h",
+                  "exact_attention_21_amd/csrc/fa_bwd_dkdv.h", "exact_attention_21_amd/csrc/fa_bwd_dkdv.hip",
+                  "exact_attention_21_amd/csrc/fa_bwd_dkdv_ilp.hip", "exact_attention_21_amd/csrc/fa_fwd.hip",
                   "exact_attention_21_amd/csrc/fa_device.h", "exact_attention_21_amd/csrc/fa_kernels.h",
                   "exact_attention_21_amd/build.py"]
 

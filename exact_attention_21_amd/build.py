@@ -18,7 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_debug.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dkdv.hip", "fa_bwd_dkdv_ilp.hip", "fa_debug.hip"]
+# per-source compiler options on top of compile_flags(): the causal d = 128
+# dK/dV kernels are built with LLVM's iterative ILP instruction scheduler
+SOURCE_FLAGS = {"fa_bwd_dkdv_ilp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 ARCH = "gfx950"
 
 
@@ -40,13 +43,18 @@ def compile_flags() -> list[str]:
             "-mllvm", "--amdgpu-mfma-vgpr-form"]
 
 
+def source_flags(src: str) -> list[str]:
+    """The full compiler options of one source file."""
+    return compile_flags() + SOURCE_FLAGS.get(src, [])
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
 
     def one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *source_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         noise = "is not a recognized feature for this target"
         err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)

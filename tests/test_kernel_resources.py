@@ -31,9 +31,9 @@ def _build_module():
 def assembly(tmp_path_factory):
     b = _build_module()
     out = {}
-    for src in ("fa_fwd.hip", "fa_bwd.hip"):
+    for src in ("fa_fwd.hip", "fa_bwd.hip", "fa_bwd_dkdv.hip", "fa_bwd_dkdv_ilp.hip"):
         dst = tmp_path_factory.mktemp("asm") / (src + ".s")
-        cmd = [b.hipcc(), *b.compile_flags(), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(dst)]
+        cmd = [b.hipcc(), *b.source_flags(src), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(dst)]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         out[src] = dst.read_text()
