@@ -25,7 +25,10 @@ and a cross-attention shape through the padded entry points) are timed too and
 reported under "sweep" (skip with --no-sweep; --sweep-only runs just those).
 
 Extra modes: --copy-ref MiB runs a plain device copy of known size (the
-reference for scaling hardware byte counters); --fwd-only times the forward alone.
+reference for scaling hardware byte counters); --gemm-ref times the vendor
+library's bf16 matrix product (torch.matmul) on large square shapes, the
+dense-bf16 rate this GPU sustains under its power limit; --fwd-only times the
+forward alone.
 """
 from __future__ import annotations
 
@@ -386,6 +389,31 @@ def copy_ref(mib, device):
     print(json.dumps({"copy_ref_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+def gemm_ref(device):
+    """bf16 C = A B through torch.matmul (2-D contiguous operands: the vendor
+    GEMM library) at n = 4096, 8192, 16384, ~20 TFLOP per shape after warm-up."""
+    import torch
+    for n in (4096, 8192, 16384):
+        a = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+        b = torch.randn(n, n, device=device, dtype=torch.bfloat16)
+        c = torch.empty(n, n, device=device, dtype=torch.bfloat16)
+        for _ in range(5):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        reps = max(5, int(2e13 / (2.0 * n ** 3)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        print(json.dumps({"gemm_ref": f"{n}x{n}x{n} bf16", "ms_per_call": ms, "calls": reps,
+                          "tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12,
+                          "frac_of_peak": 2.0 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}), flush=True)
+        del a, b, c
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,6 +423,7 @@ def main():
     ap.add_argument("--cpu-bwd-max-n", type=int, default=8192,
                     help="largest N for which the CPU baseline includes the backward")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB")
+    ap.add_argument("--gemm-ref", action="store_true", help="time the vendor bf16 GEMM (power-limited dense rate)")
     ap.add_argument("--fwd-only", action="store_true", help="time only the forward (diagnostics)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the other configurations' timings")
     ap.add_argument("--sweep-only", action="store_true", help="time only the other configurations")
@@ -415,6 +444,9 @@ def main():
     torch.cuda.set_device(device)
     if args.copy_ref:
         copy_ref(args.copy_ref, device)
+        return
+    if args.gemm_ref:
+        gemm_ref(device)
         return
 
     if args.sweep_only:
