@@ -713,11 +713,15 @@ hipError_t launch_fwd(const FwdParams &p, int dtype, int d, int causal, int qb, 
   if (dtype == 1) {
     FA_FWD_CASE(BF16, 128, FWD_QB_D128)
     FA_FWD_CASE(BF16, 64, 1)
-    FA_FWD_CASE(BF16, 64, 2)
+#if FWD_QB_D64 != 1
+    FA_FWD_CASE(BF16, 64, FWD_QB_D64)
+#endif
   } else {
     FA_FWD_CASE(F16, 128, FWD_QB_D128)
     FA_FWD_CASE(F16, 64, 1)
-    FA_FWD_CASE(F16, 64, 2)
+#if FWD_QB_D64 != 1
+    FA_FWD_CASE(F16, 64, FWD_QB_D64)
+#endif
   }
 #undef FA_FWD_CASE
   return hipErrorInvalidValue;
