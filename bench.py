@@ -45,6 +45,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+SWEEP_WARMUP_S = 0.05  # seconds of untimed work per sweep configuration before its timed steps
 WORKLOAD = dict(name="c3_fwd_bwd_causal_n8192_d128_bf16", B=4, H=32, N=8192, d=128, dtype="bf16",
                 causal=True)
 
@@ -296,18 +297,34 @@ def sweep(fa, device, steps, warmup, only=None):
         ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=device)
         scale = 1 / math.sqrt(d)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        for i in range(warmup + steps):
-            e = ev[i - warmup] if i >= warmup else None
-            if e:
-                e[0].record(stream)
+        # untimed warm-up of at least `warmup` steps and SWEEP_WARMUP_S seconds:
+        # the power-limited clock takes milliseconds to settle after the
+        # previous configuration's load
+        t_warm, i = time.perf_counter(), 0
+        while i < warmup or time.perf_counter() - t_warm < SWEEP_WARMUP_S:
+            if drop > 0:
+                fa.fa_fwd_dropout(q, k, v, o, lse, lq, lk, scale, causal, drop, c["seed"], i, stream)
+                fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, lq, lk, scale, causal, drop, c["seed"], i,
+                                  ws, stream)
+            elif padded:
+                fa.fa_fwd_padded(q, k, v, o, lse, lq, lk, scale, causal, stream)
+                fa.fa_bwd_padded(q, k, v, o, do, lse, dq, dk, dv, lq, lk, scale, causal, ws, stream)
+            else:
+                fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
+                fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, ws, stream)
+            i += 1
+            if i % max(1, warmup) == 0:
+                torch.cuda.synchronize()
+        for i in range(warmup, warmup + steps):
+            e = ev[i - warmup]
+            e[0].record(stream)
             if drop > 0:
                 fa.fa_fwd_dropout(q, k, v, o, lse, lq, lk, scale, causal, drop, c["seed"], i, stream)
             elif padded:
                 fa.fa_fwd_padded(q, k, v, o, lse, lq, lk, scale, causal, stream)
             else:
                 fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
-            if e:
-                e[1].record(stream)
+            e[1].record(stream)
             if drop > 0:
                 fa.fa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, lq, lk, scale, causal, drop, c["seed"], i,
                                   ws, stream)
@@ -315,8 +332,7 @@ def sweep(fa, device, steps, warmup, only=None):
                 fa.fa_bwd_padded(q, k, v, o, do, lse, dq, dk, dv, lq, lk, scale, causal, ws, stream)
             else:
                 fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, ws, stream)
-            if e:
-                e[2].record(stream)
+            e[2].record(stream)
         torch.cuda.synchronize()
         if padded:
             pairs = sum(visible_pairs(int(lens[b]) if lens is not None else N,
