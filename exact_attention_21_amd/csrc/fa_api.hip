@@ -114,7 +114,7 @@ int check_common(int B, int H, int N, int d, int causal, int dtype) {
 // Query rows per forward workgroup = 128 * qb (32 * qb rows per wave): one
 // block per wave at d = 128 (register budget) and, by default, at d = 64 too
 // (FWD_QB_D64; two blocks at occupancy 2 measured slower than one at 4).
-int fwd_qb(int N, int d) { return d == 128 ? FWD_QB_D128 : (N > 128 ? FWD_QB_D64 : 1); }
+int fwd_qb(int N, int d) { return d == 128 ? 1 : (N > 128 ? FWD_QB_D64 : 1); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -155,7 +155,7 @@ struct SplitPlan {
 SplitPlan split_plan(int B, int H, int Nq, int Nk, int d) {
   constexpr long long kResident = 256 * 3;
   SplitPlan sp;
-  sp.bm = 128 * (d == 128 ? FWD_QB_D128 : 1);
+  sp.bm = 128;
   sp.n_qtiles = (Nq + sp.bm - 1) / sp.bm;
   const long long units = (long long)B * H * sp.n_qtiles;
   const long long most = ((long long)Nk + 255) / 256;

@@ -62,19 +62,6 @@ constexpr float LAZY_TAU = 8.0f;  // log2 growth of a row max that forces a resc
 constexpr float LAZY_BOUND = 256.0f;  // 2^LAZY_TAU: largest probability kept without a rescale
 constexpr float M_FLOOR = -1e30f; // initial running max (log2 units)
 
-// o *= a for an accumulator that lives in AGPRs (rare path): read, scale and
-// write back each register without moving the accumulator out of AGPRs.
-__device__ __forceinline__ void scale_acc_agpr(f32x16 &acc, float a) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float x = acc[i], tmp;
-    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                 : "+a"(x), "=&v"(tmp)
-                 : "v"(a));
-    acc[i] = x;
-  }
-}
-
 // XOR swizzles of the 16-byte chunk index within a tile row.
 template <int D>
 __device__ __forceinline__ int swz_k(int row) {
@@ -99,7 +86,7 @@ static_assert(swz_v_period16<64>() && swz_v_period16<128>(), "V swizzle must rep
 // waves per SIMD: two query blocks per wave need the registers of occupancy 2
 #define FWD_OCC(D, QB, DROP) ((QB) == 2 ? 2 : (D) == 64 ? FWD_WAVES_D64 : FWD_WAVES_PER_SIMD)
 
-template <class T, int D, int QB, bool CAUSAL, bool O_IN_AGPR, bool DROP, bool SPLIT>
+template <class T, int D, int QB, bool CAUSAL, bool DROP, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FWD_OCC(D, QB, DROP), FWD_OCC(D, QB, DROP))))
 void fwd_kernel(FwdParams p) {
   constexpr int BN = FWD_BN;
@@ -367,19 +354,10 @@ void fwd_kernel(FwdParams p) {
     }
   };
   auto rescale_o = [&](const float (&alpha)[QB]) {
-    if constexpr (O_IN_AGPR) {
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // MFMA results settle before reads
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int c = 0; c < ND32; ++c) scale_acc_agpr(oacc[qb][c], alpha[qb]);
-      asm volatile("s_nop 4");
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int c = 0; c < ND32; ++c) oacc[qb][c] *= alpha[qb];
-    }
+      for (int c = 0; c < ND32; ++c) oacc[qb][c] *= alpha[qb];
   };
 
   // K(t) and V(t) go to ring slot SL
@@ -657,16 +635,15 @@ __global__ __launch_bounds__(256) void fwd_decode_kernel(FwdParams p) {
 template <class T, int D, int QB, bool C>
 static hipError_t launch_fwd_t(const FwdParams &p, int grid, hipStream_t st) {
   if (p.drop.p8 != 0)
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, true, false>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, true, false>), dim3(grid), dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, false, false>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, false, false>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 template <class T, int D, bool C>
 static hipError_t launch_split_t(const FwdParams &p, int grid, hipStream_t st) {
-  constexpr int QB = D == 128 ? FWD_QB_D128 : 1;
-  hipLaunchKernelGGL((fwd_kernel<T, D, QB, C, FWD_O_IN_AGPR, false, true>), dim3(grid), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, 1, C, false, true>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -711,13 +688,13 @@ hipError_t launch_fwd(const FwdParams &p, int dtype, int d, int causal, int qb, 
                   : launch_fwd_t<TT, DD, QQ, false>(p, grid, st);                     \
   }
   if (dtype == 1) {
-    FA_FWD_CASE(BF16, 128, FWD_QB_D128)
+    FA_FWD_CASE(BF16, 128, 1)
     FA_FWD_CASE(BF16, 64, 1)
 #if FWD_QB_D64 != 1
     FA_FWD_CASE(BF16, 64, FWD_QB_D64)
 #endif
   } else {
-    FA_FWD_CASE(F16, 128, FWD_QB_D128)
+    FA_FWD_CASE(F16, 128, 1)
     FA_FWD_CASE(F16, 64, 1)
 #if FWD_QB_D64 != 1
     FA_FWD_CASE(F16, 64, FWD_QB_D64)

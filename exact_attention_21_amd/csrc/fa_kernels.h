@@ -9,20 +9,11 @@ namespace fa {
 
 // Keys per K/V tile (one pipeline step) of the forward kernel.
 constexpr int FWD_BN = 32;
-// Query blocks of 32 rows per wave for head dim 128, and whether the output
-// accumulator is kept in AGPRs (set together with the compiler's MFMA register
-// form for fa_fwd.hip).
 #ifndef FWD_NSLOT_D128
 #define FWD_NSLOT_D128 3  // K/V ring slots of the d = 128 forward without dropout (tiles loaded NSLOT - 1 steps ahead)
 #endif
 #ifndef FWD_NSLOT_SPLIT
 #define FWD_NSLOT_SPLIT 3  // the same for the split forward (decode shapes)
-#endif
-#ifndef FWD_QB_D128
-#define FWD_QB_D128 1
-#endif
-#ifndef FWD_O_IN_AGPR
-#define FWD_O_IN_AGPR (FWD_QB_D128 == 2)
 #endif
 // Waves per SIMD the forward kernel is compiled for (occupancy target).
 #ifndef FWD_WAVES_PER_SIMD
