@@ -437,43 +437,82 @@ void fwd_kernel(FwdParams p) {
   uint16_t *Oh = reinterpret_cast<uint16_t *>(p.o) + qoff;
   float *Lh = p.lse + (size_t)bh * Nq;
   const size_t pbase = SPLIT ? ((size_t)bh * p.nsplit + split) * Nq : 0;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = lrun[qb] + xhalf(lrun[qb]);
-    const int row = wr0 + qb * 32 + l32;
+  if constexpr (!SPLIT && QB == 1) {
+    // O goes out through LDS: each wave writes its 32 x D tile (16-bit) into
+    // a ring slot of its own, then stores whole rows, 16 bytes per lane and
+    // 64 / (D / 8) rows per instruction, instead of scattered 8-byte pieces
+    // (the scattered stores competed with the other workgroups' tile loads).
+    // The barrier: every wave's trailing loads have landed in the ring.
+    barrier_only();
+    static_assert(32 * RB <= TB, "a wave's output tile fits one ring slot");
+    char *stage = w == 0 ? k_slot0 : w == 1 ? k_slot1 : w == 2 ? v_slot0 : v_slot1;
+    const float lt = lrun[0] + xhalf(lrun[0]);
+    const int row = wr0 + l32;
     // padding rows and rows that see no key (row sum exactly 0): O = 0,
     // LSE = -inf; a live row's sum is >= 1 (its largest term is taken against
     // a running max no larger than the row's max), and NaN stays NaN
     const bool live = row < Lq && lt != 0.f;
     const float inv = (DROP ? p.drop.scale : 1.f) / lt;  // kept weights are scaled by 256 / (256 - p8)
-    if (SPLIT && row < Nq) {
 #pragma unroll
-      for (int c = 0; c < ND32; ++c)
+    for (int c = 0; c < ND32; ++c)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int dcol = c * 32 + 8 * rg + 4 * hi;
-          f32x4 st = {0.f, 0.f, 0.f, 0.f};
-          if (live)
-            st = f32x4{oacc[qb][c][4 * rg] * inv, oacc[qb][c][4 * rg + 1] * inv,
-                       oacc[qb][c][4 * rg + 2] * inv, oacc[qb][c][4 * rg + 3] * inv};
-          *reinterpret_cast<f32x4 *>(p.opart + (pbase + row) * D + dcol) = st;
+      for (int rg = 0; rg < 4; ++rg) {
+        u32x2 st = {0u, 0u};
+        if (live) {
+          st[0] = T::pack(oacc[0][c][4 * rg + 0] * inv, oacc[0][c][4 * rg + 1] * inv);
+          st[1] = T::pack(oacc[0][c][4 * rg + 2] * inv, oacc[0][c][4 * rg + 3] * inv);
         }
-      if (hi == 0)
-        p.lpart[pbase + row] = live ? (mrun[qb] + fast_log2(lt)) * 0.69314718055994531f : -__builtin_inff();
-    } else if (!SPLIT && row < Nq) {
+        // columns c * 32 + 8 rg + 4 hi .. + 3: 16-byte chunk 4 c + rg, XOR-swizzled by row
+        *reinterpret_cast<u32x2 *>(stage + l32 * RB + (((4 * c + rg) ^ (l32 & (CPR - 1))) << 4) + 8 * hi) = st;
+      }
+    if (hi == 0 && row < Nq) Lh[row] = live ? (mrun[0] + fast_log2(lt)) * 0.69314718055994531f : -__builtin_inff();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is in LDS before it is read back
+    constexpr int RPI = 64 / CPR;  // rows per store instruction
 #pragma unroll
-      for (int c = 0; c < ND32; ++c)
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = it * RPI + lane / CPR, ch = lane % CPR;
+      const u32x4 v = lds_read16(stage + r * RB + ((ch ^ (r & (CPR - 1))) << 4));
+      if (wr0 + r < Nq) *reinterpret_cast<u32x4 *>(Oh + (size_t)(wr0 + r) * D + ch * 8) = v;
+    }
+  } else {
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int dcol = c * 32 + 8 * rg + 4 * hi;
-          u32x2 st = {0u, 0u};
-          if (live) {
-            st[0] = T::pack(oacc[qb][c][4 * rg + 0] * inv, oacc[qb][c][4 * rg + 1] * inv);
-            st[1] = T::pack(oacc[qb][c][4 * rg + 2] * inv, oacc[qb][c][4 * rg + 3] * inv);
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = lrun[qb] + xhalf(lrun[qb]);
+      const int row = wr0 + qb * 32 + l32;
+      // padding rows and rows that see no key (row sum exactly 0): O = 0,
+      // LSE = -inf; a live row's sum is >= 1 (its largest term is taken against
+      // a running max no larger than the row's max), and NaN stays NaN
+      const bool live = row < Lq && lt != 0.f;
+      const float inv = (DROP ? p.drop.scale : 1.f) / lt;  // kept weights are scaled by 256 / (256 - p8)
+      if (SPLIT && row < Nq) {
+#pragma unroll
+        for (int c = 0; c < ND32; ++c)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int dcol = c * 32 + 8 * rg + 4 * hi;
+            f32x4 st = {0.f, 0.f, 0.f, 0.f};
+            if (live)
+              st = f32x4{oacc[qb][c][4 * rg] * inv, oacc[qb][c][4 * rg + 1] * inv,
+                         oacc[qb][c][4 * rg + 2] * inv, oacc[qb][c][4 * rg + 3] * inv};
+            *reinterpret_cast<f32x4 *>(p.opart + (pbase + row) * D + dcol) = st;
           }
-          *reinterpret_cast<u32x2 *>(Oh + (size_t)row * D + dcol) = st;
-        }
-      if (hi == 0) Lh[row] = live ? (mrun[qb] + fast_log2(lt)) * 0.69314718055994531f : -__builtin_inff();
+        if (hi == 0)
+          p.lpart[pbase + row] = live ? (mrun[qb] + fast_log2(lt)) * 0.69314718055994531f : -__builtin_inff();
+      } else if (!SPLIT && row < Nq) {
+#pragma unroll
+        for (int c = 0; c < ND32; ++c)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int dcol = c * 32 + 8 * rg + 4 * hi;
+            u32x2 st = {0u, 0u};
+            if (live) {
+              st[0] = T::pack(oacc[qb][c][4 * rg + 0] * inv, oacc[qb][c][4 * rg + 1] * inv);
+              st[1] = T::pack(oacc[qb][c][4 * rg + 2] * inv, oacc[qb][c][4 * rg + 3] * inv);
+            }
+            *reinterpret_cast<u32x2 *>(Oh + (size_t)row * D + dcol) = st;
+          }
+        if (hi == 0) Lh[row] = live ? (mrun[qb] + fast_log2(lt)) * 0.69314718055994531f : -__builtin_inff();
+      }
     }
   }
 }
