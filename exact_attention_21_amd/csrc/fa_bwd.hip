@@ -368,24 +368,26 @@ void bwd_dq_kernel(BwdParams p) {
   }
   wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
-  // dQ = scale dQ^T^T, rounded to 16 bits (0 for padding rows)
-  if (qrow < Nq) {
-    uint16_t *dQh = reinterpret_cast<uint16_t *>(p.dq) + qoff;
-    const bool live = qrow < Lq;  // padding rows store zeros
-    const float sc = p.scale;
+  // dQ = scale dQ^T^T, rounded to 16 bits (0 for padding rows), leaving
+  // through LDS as whole rows (stage_put, stage_store_rows); the barrier: every wave's
+  // trailing loads have landed in the ring, whose slots are free now
+  barrier_only();
+  static_assert(32 * RB <= TB, "a wave's dQ tile fits one ring slot");
+  char *stage = w == 0 ? k_slot0 : w == 1 ? k_slot1 : w == 2 ? v_slot0 : v_slot1;
+  const bool live = qrow < Lq;  // padding rows store zeros
+  const float sc = p.scale;
 #pragma unroll
-    for (int c = 0; c < ND32; ++c)
+  for (int c = 0; c < ND32; ++c)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int dcol = c * 32 + 8 * rg + 4 * hi;
-        u32x2 st = {0u, 0u};
-        if (live) {
-          st[0] = T::pack(dqacc[c][4 * rg] * sc, dqacc[c][4 * rg + 1] * sc);
-          st[1] = T::pack(dqacc[c][4 * rg + 2] * sc, dqacc[c][4 * rg + 3] * sc);
-        }
-        *reinterpret_cast<u32x2 *>(dQh + (size_t)qrow * D + dcol) = st;
+    for (int rg = 0; rg < 4; ++rg) {
+      u32x2 st = {0u, 0u};
+      if (live) {
+        st[0] = T::pack(dqacc[c][4 * rg] * sc, dqacc[c][4 * rg + 1] * sc);
+        st[1] = T::pack(dqacc[c][4 * rg + 2] * sc, dqacc[c][4 * rg + 3] * sc);
       }
-  }
+      stage_put<D>(stage, c, rg, st, lane);
+    }
+  stage_store_rows<D>(stage, reinterpret_cast<uint16_t *>(p.dq) + qoff, wr0, Nq, lane);
 }
 
 

@@ -295,13 +295,46 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   wait_vmcnt<0>();  // the trailing (zero-filled) loads have landed before exit
 
-  // dK = scale dK^T^T, dV = dV^T^T, rounded to 16 bits (0 for padding keys)
-  if (key < Nk) {
+  // dK = scale dK^T^T, dV = dV^T^T, rounded to 16 bits (0 for padding keys),
+  // each leaving through LDS as whole rows (stage_put, stage_store_rows); the
+  // barrier: every wave's trailing loads have landed in the ring, whose slots
+  // are free now (two waves' tiles per slot).  With dropout the tiles are
+  // stored directly (staged, the causal d = 128 kernel spilled under its
+  // instruction scheduler).
+  const bool live = key < Lk;  // padding keys store zeros (their sums are meaningless)
+  const float sc = p.scale;
+  const float sd = DROP ? p.drop.scale : 1.f;  // dV = sum (P * keep) dO * 256 / (256 - p8)
+  if constexpr (!DROP) {
+    barrier_only();
+    static_assert(2 * 32 * RB <= SLOT, "two waves' tiles fit one ring slot");
+    char *stage = (w < 2 ? slot0 : slot1) + (w & 1) * 32 * RB;
+#pragma unroll
+    for (int c = 0; c < ND32; ++c)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        u32x2 st = {0u, 0u};
+        if (live) {
+          st[0] = T::pack(dkacc[c][4 * rg] * sc, dkacc[c][4 * rg + 1] * sc);
+          st[1] = T::pack(dkacc[c][4 * rg + 2] * sc, dkacc[c][4 * rg + 3] * sc);
+        }
+        stage_put<D>(stage, c, rg, st, lane);
+      }
+    stage_store_rows<D>(stage, reinterpret_cast<uint16_t *>(p.dk) + koff, kw0, Nk, lane);
+#pragma unroll
+    for (int c = 0; c < ND32; ++c)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        u32x2 st = {0u, 0u};
+        if (live) {
+          st[0] = T::pack(dvacc[c][4 * rg] * sd, dvacc[c][4 * rg + 1] * sd);
+          st[1] = T::pack(dvacc[c][4 * rg + 2] * sd, dvacc[c][4 * rg + 3] * sd);
+        }
+        stage_put<D>(stage, c, rg, st, lane);
+      }
+    stage_store_rows<D>(stage, reinterpret_cast<uint16_t *>(p.dv) + koff, kw0, Nk, lane);
+  } else if (key < Nk) {
     uint16_t *dKh = reinterpret_cast<uint16_t *>(p.dk) + koff;
     uint16_t *dVh = reinterpret_cast<uint16_t *>(p.dv) + koff;
-    const bool live = key < Lk;  // padding keys store zeros (their sums are meaningless)
-    const float sc = p.scale;
-    const float sd = DROP ? p.drop.scale : 1.f;  // dV = sum (P * keep) dO * 256 / (256 - p8)
 #pragma unroll
     for (int c = 0; c < ND32; ++c)
 #pragma unroll

@@ -205,6 +205,35 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Output tiles leave through LDS.  A wave's 32 x D tile of 16-bit values
+// comes out of a transposed 32x32 accumulator with lane l holding row l % 32,
+// columns c * 32 + 8 rg + 4 (l / 32) .. + 3 as two packed pairs per (c, rg).
+// Stored directly, every store instruction would write 16 bytes into each of
+// 32 rows; instead each pair goes to `stage` (32 * D * 2 bytes of LDS that
+// only this wave uses, 16-byte chunks XOR-swizzled by row: stage_put), and
+// the rows come back one 16-byte piece per lane, so that each store writes
+// whole rows (stage_store_rows).
+template <int D>
+__device__ __forceinline__ void stage_put(char *stage, int c, int rg, u32x2 v, int lane) {
+  constexpr int RB = D * 2, CPR = RB / 16;  // row bytes, 16-byte chunks per row
+  const int l32 = lane & 31, hi = lane >> 5;
+  *reinterpret_cast<u32x2 *>(stage + l32 * RB + (((4 * c + rg) ^ (l32 & (CPR - 1))) << 4) + 8 * hi) = v;
+}
+// Rows row0 .. row0 + 31 of the row-major [rows][D] array dst, those below
+// nrows, from the staged tile; the stage may be reused after it returns.
+template <int D>
+__device__ __forceinline__ void stage_store_rows(const char *stage, uint16_t *dst, int row0, int nrows, int lane) {
+  constexpr int RB = D * 2, CPR = RB / 16, RPI = 64 / CPR;  // rows per store
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is in LDS before it is read back
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = it * RPI + lane / CPR, ch = lane % CPR;
+    const u32x4 x = lds_read16(stage + r * RB + ((ch ^ (r & (CPR - 1))) << 4));
+    if (row0 + r < nrows) *reinterpret_cast<u32x4 *>(dst + (size_t)(row0 + r) * D + ch * 8) = x;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the stage is written again
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }   // v_log_f32 (base 2)
 

@@ -438,11 +438,9 @@ void fwd_kernel(FwdParams p) {
   float *Lh = p.lse + (size_t)bh * Nq;
   const size_t pbase = SPLIT ? ((size_t)bh * p.nsplit + split) * Nq : 0;
   if constexpr (!SPLIT && QB == 1) {
-    // O goes out through LDS: each wave writes its 32 x D tile (16-bit) into
-    // a ring slot of its own, then stores whole rows, 16 bytes per lane and
-    // 64 / (D / 8) rows per instruction, instead of scattered 8-byte pieces
-    // (the scattered stores competed with the other workgroups' tile loads).
-    // The barrier: every wave's trailing loads have landed in the ring.
+    // O leaves through LDS as whole rows (stage_put, stage_store_rows); the barrier:
+    // every wave's trailing loads have landed in the ring, whose slots are
+    // free now (one per wave)
     barrier_only();
     static_assert(32 * RB <= TB, "a wave's output tile fits one ring slot");
     char *stage = w == 0 ? k_slot0 : w == 1 ? k_slot1 : w == 2 ? v_slot0 : v_slot1;
@@ -462,18 +460,10 @@ void fwd_kernel(FwdParams p) {
           st[0] = T::pack(oacc[0][c][4 * rg + 0] * inv, oacc[0][c][4 * rg + 1] * inv);
           st[1] = T::pack(oacc[0][c][4 * rg + 2] * inv, oacc[0][c][4 * rg + 3] * inv);
         }
-        // columns c * 32 + 8 rg + 4 hi .. + 3: 16-byte chunk 4 c + rg, XOR-swizzled by row
-        *reinterpret_cast<u32x2 *>(stage + l32 * RB + (((4 * c + rg) ^ (l32 & (CPR - 1))) << 4) + 8 * hi) = st;
+        stage_put<D>(stage, c, rg, st, lane);
       }
     if (hi == 0 && row < Nq) Lh[row] = live ? (mrun[0] + fast_log2(lt)) * 0.69314718055994531f : -__builtin_inff();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is in LDS before it is read back
-    constexpr int RPI = 64 / CPR;  // rows per store instruction
-#pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int r = it * RPI + lane / CPR, ch = lane % CPR;
-      const u32x4 v = lds_read16(stage + r * RB + ((ch ^ (r & (CPR - 1))) << 4));
-      if (wr0 + r < Nq) *reinterpret_cast<u32x4 *>(Oh + (size_t)(wr0 + r) * D + ch * 8) = v;
-    }
+    stage_store_rows<D>(stage, Oh, wr0, Nq, lane);
   } else {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
