@@ -138,8 +138,9 @@ void bwd_dq_kernel(BwdParams p) {
   // resources end at the valid rows: padding queries and keys read as zeros
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const uint16_t *>(p.q) + qoff, (uint32_t)Lq * RB);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const uint16_t *>(p.dout) + qoff, (uint32_t)Lq * RB);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const uint16_t *>(p.k) + koff, (uint32_t)Lk * RB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const uint16_t *>(p.v) + koff, (uint32_t)Lk * RB);
+  const char *k_head = reinterpret_cast<const char *>(p.k) + koff * 2;
+  const char *v_head = reinterpret_cast<const char *>(p.v) + koff * 2;
+  const uint32_t kv_bytes = (uint32_t)Lk * RB;
 
   const int kend = i0 >= Lq ? 0 : CAUSAL ? max(0, min(Lk, i0 + BM + shift)) : Lk;
   const int nt = (kend + BN - 1) / BN;
@@ -212,14 +213,16 @@ void bwd_dq_kernel(BwdParams p) {
   // tile t goes to ring slot SL (tiles outside [0, nt) load as zeros)
   auto issue_step = [&](int t, auto slot) {
     constexpr int SL = decltype(slot)::value;
+    // a resource per tile (scalar arithmetic): the per-lane offsets stay loop-invariant
     const bool ok = t >= 0 && t < nt;
-    const uint32_t base = ok ? (uint32_t)t * TB : 0x80000000u;
+    const __amdgpu_buffer_rsrc_t rkt = tile_rsrc(k_head, (uint32_t)t * TB, kv_bytes, ok);
+    const __amdgpu_buffer_rsrc_t rvt = tile_rsrc(v_head, (uint32_t)t * TB, kv_bytes, ok);
     char *ks = SL == 0 ? k_slot0 : SL == 1 ? k_slot1 : k_slot2;
     char *vs = SL == 0 ? v_slot0 : SL == 1 ? v_slot1 : v_slot2;
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
-      dma16(rk, ks + (w * BPW + j) * 1024, base + dk_off[j]);
-      dma16(rv, vs + (w * BPW + j) * 1024, base + dv_off[j]);
+      dma16(rkt, ks + (w * BPW + j) * 1024, dk_off[j]);
+      dma16(rvt, vs + (w * BPW + j) * 1024, dv_off[j]);
     }
   };
 

@@ -175,6 +175,23 @@ __device__ __forceinline__ const char *uniform_ptr(const char *ptr) {
   return reinterpret_cast<const char *>(((uint64_t)hi << 32) | lo);
 }
 
+// Buffer resource of one tile of a tensor whose first `valid` bytes at `base`
+// hold data: it starts at byte tb and ends where the valid bytes end (rows
+// past it read as zeros), so the per-lane offsets of the tile's loads stay
+// loop-invariant; ok = false gives an empty record (every load reads zeros).
+// The arguments are wave-uniform; unsigned, so that a tensor may span up to
+// 2^32 - 1 bytes.  The record size valid - tb, or 0 where the unsigned
+// subtraction borrows (tb >= valid), takes two scalar instructions; written in
+// C the compiler takes the saturating subtraction to the vector ALU (a move, a
+// clamped subtraction, a select and a readfirstlane per tile).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, uint32_t tb, uint32_t valid, bool ok) {
+  const uint32_t t = __builtin_amdgcn_readfirstlane(ok ? tb : 0u);
+  const uint32_t v = __builtin_amdgcn_readfirstlane(ok ? valid : 0u);
+  uint32_t n;
+  asm("s_sub_u32 %0, %1, %2\n\ts_cselect_b32 %0, 0, %0" : "=&s"(n) : "s"(v), "s"(t) : "scc");
+  return make_rsrc(uniform_ptr(base + t), n);
+}
+
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }

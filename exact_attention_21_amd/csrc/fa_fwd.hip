@@ -183,12 +183,7 @@ void fwd_kernel(FwdParams p) {
   const char *v_head = reinterpret_cast<const char *>(p.v) + koff * 2;
   const uint32_t kv_bytes = (uint32_t)Lk * RB;
   auto issue_tile = [&](const char *head, int t, char *slot, const uint32_t (&offs)[BPW]) {
-    const bool ok = t >= t_beg && t < t_end;
-    // the values are wave-uniform; readfirstlane keeps them (and the resource)
-    // in SGPRs.  Unsigned: a head's K or V may span up to 2^32 - 1 bytes.
-    const uint32_t tb = __builtin_amdgcn_readfirstlane(ok ? (uint32_t)t * TB : 0u);
-    const uint32_t n = __builtin_amdgcn_readfirstlane(ok && tb < kv_bytes ? kv_bytes - tb : 0u);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(head + tb), n);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(head, (uint32_t)t * TB, kv_bytes, t >= t_beg && t < t_end);
 #pragma unroll
     for (int j = 0; j < BPW; ++j) dma16(r, slot + (w * BPW + j) * 1024, offs[j]);
   };
@@ -335,13 +330,15 @@ void fwd_kernel(FwdParams p) {
     }
     return grow_any;
   };
-  // O^T += V(t)^T P(t)^T, V(t) in ring slot SL
+  // O^T += V(t)^T P(t)^T, V(t) in ring slot SL; the 16-key halves outermost, so
+  // that consecutive MFMAs share their B operand (each output block still adds
+  // its first half before its second)
   auto stage_pv = [&](auto slot, const uint32_t (&pk)[QB][8]) {
     const char *vs = vslot(slot);
 #pragma unroll
-    for (int c = 0; c < ND32; ++c) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int c = 0; c < ND32; ++c) {
         const u32x2 a0 = lds_read_tr4(vs + kb * 16 * RB + v_addr[c][0]);
         const u32x2 a1 = lds_read_tr4(vs + kb * 16 * RB + v_addr[c][1]);
         const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
