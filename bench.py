@@ -342,13 +342,16 @@ def sweep(fa, device, steps, warmup, only=None):
             f_bwd = 2.5 * f_fwd
         else:
             f_fwd, f_bwd = nominal_flop(B, H, N, d, causal)
-        fms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-        bms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+        fts = [e[0].elapsed_time(e[1]) for e in ev]
+        bts = [e[1].elapsed_time(e[2]) for e in ev]
+        fms, bms = sum(fts) / steps, sum(bts) / steps
         res[name] = {"B": B, "H": H, "N": N, "Nk": Nk, "d": d, "dtype": c["dtype"], "causal": causal,
                      "dropout": drop,
                      "lengths": None if lens is None else [int(x) for x in lens],
                      "fwd_ms": fms, "fwd_tflops": f_fwd / (fms * 1e-3) / 1e12,
-                     "bwd_ms": bms, "bwd_tflops": f_bwd / (bms * 1e-3) / 1e12}
+                     "fwd_ms_median": statistics.median(fts), "fwd_ms_min": min(fts),
+                     "bwd_ms": bms, "bwd_tflops": f_bwd / (bms * 1e-3) / 1e12,
+                     "bwd_ms_median": statistics.median(bts), "bwd_ms_min": min(bts)}
         log(f"[bench] sweep {name}: fwd {fms:.3f} ms ({res[name]['fwd_tflops']:.0f} TFLOP/s)  "
             f"bwd {bms:.3f} ms ({res[name]['bwd_tflops']:.0f} TFLOP/s nominal)")
         if not padded:
