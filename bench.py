@@ -45,7 +45,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
-SWEEP_WARMUP_S = 0.05  # seconds of untimed work per sweep configuration before its timed steps
+SWEEP_WARMUP_S = 0.5  # seconds of untimed work per sweep configuration before its timed steps
 WORKLOAD = dict(name="c3_fwd_bwd_causal_n8192_d128_bf16", B=4, H=32, N=8192, d=128, dtype="bf16",
                 causal=True)
 
