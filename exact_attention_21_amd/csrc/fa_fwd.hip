@@ -21,10 +21,11 @@
 // transposing read ds_read_b64_tr_b16.  Exponentials are base 2 with log2(e)
 // folded into the score scale.
 //
-// K/V tiles reach LDS by direct buffer->LDS loads (no staging registers) one
-// step ahead, into rings of two slots (one LDS object per slot, so that the
-// compiler sees the load into one slot and the reads of the other do not
-// alias).  Tiles are stored with unpadded rows and an XOR swizzle of the
+// K/V tiles reach LDS by direct buffer->LDS loads (no staging registers) into
+// rings of two or three slots, one or two steps ahead (one LDS object per
+// slot, so that the compiler sees the load into one slot and the reads of the
+// others do not alias); each tile's buffer resource starts at the tile, so the
+// per-lane load offsets stay loop-invariant.  Tiles are stored with unpadded rows and an XOR swizzle of the
 // 16-byte chunk index chosen per access pattern (K: chunk ^ (row & 15) at
 // d = 128, conflict-free for the 16-byte fragment reads; V: a swizzle of row
 // bits 0..3 conflict-free for the transposing reads).  Rows past the valid
